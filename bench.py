@@ -1,0 +1,237 @@
+"""Benchmark of the hybrid Top-k + Top-p block-sparse attention layer on one MI355X.
+
+One step = the whole hot path on one synthetic layer with inputs resident in HBM:
+build_mask (pool + select) -> sparse forward (with the O residual) -> sparse backward
+(D and column lists, dK/dV, dQ).  Default workload: the Wan2.1-1.3B-480p-shaped layer
+(B=1, H=12, N=32760 on a 21x30x52 grid, d=128, blocks 128x64, k=5 %, p=0.9).
+
+Prints one JSON line with the step time (ms/layer), the per-stage times measured with
+HIP events on the launch stream, the roofline of the dominant kernel, a dense-mask run
+of the same kernels and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd ms/layer & MFMA util at 95% block sparsity, N=32760 H=12 d=128"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kept_pairs_weight(kv_idx, kv_cnt, N, bq, bk):
+    """sum over kept (i, j) of n_i * m_j (valid rows times valid keys)."""
+    B, H, nqb, nkb = kv_idx.shape
+    n_i = np.minimum(bq, N - np.arange(nqb) * bq).astype(np.int64)
+    m_j = np.minimum(bk, N - np.arange(nkb) * bk).astype(np.int64)
+    total = 0
+    for b in range(B):
+        for h in range(H):
+            for i in range(nqb):
+                c = int(kv_cnt[b, h, i])
+                total += int(n_i[i]) * int(m_j[kv_idx[b, h, i, :c]].sum())
+    return total
+
+
+def cpu_oracle_baseline(g, w, lists, budget_s: float):
+    """Time the CPU oracle on a bounded sample of the layer and scale to ms/layer.
+
+    The mask is computed for every head; forward + backward run query block by query
+    block (all heads, a fixed interleaved order) until the time budget is spent, and the
+    per-block time is scaled to the whole layer.
+    """
+    from oracle import spa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count()
+    f = {n: O.widen_bf16(g[n]) for n in ("q", "k", "v", "do")}
+    t0 = time.perf_counter()
+    O.build_mask(f["q"], f["k"], w.blk_q, w.blk_k, w.k_frac, w.p)
+    t_mask = time.perf_counter() - t0
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    order = [(heads[x % len(heads)], (x * 37) % w.n_qblk)
+             for x in range(len(heads) * w.n_qblk)]
+    done = 0
+    t0 = time.perf_counter()
+    for (bh, i) in order:
+        O.sparse_attn_fwd(f["q"], f["k"], f["v"], lists, w.blk_q, w.blk_k, heads=[bh],
+                          qblocks=[i])
+        O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, w.blk_q, w.blk_k, heads=[bh],
+                          qblocks=[i])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t_attn = time.perf_counter() - t0
+    per_layer = t_mask + t_attn / done * len(order)
+    return {
+        "value": per_layer * 1e3, "unit": "ms/layer", "cores": int(threads), "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: mask of all {len(heads)} heads ({t_mask:.2f} s) and "
+                   f"fwd+bwd of {done} of {len(order)} (head, query block) units "
+                   f"({t_attn:.2f} s), scaled linearly to the whole layer"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan13b_480p")
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of CPU oracle work to time for the baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer shards by "
+              "(batch, head) with no exchange, so run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_pooled_amd as spa
+    from block_sparse_attention_pooled_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    spa.load_library()
+    w = synth.WORKLOADS[args.workload]
+    B, H, N, d = w.shape()
+    log(f"[bench] generating {w.name} {w.shape()}")
+    g = synth.generate(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (torch.from_numpy(g[n].view(np.int16)).view(torch.bfloat16).to(dev)
+                   for n in ("q", "k", "v", "do"))
+    nqb, nkb = w.n_qblk, w.n_kblk
+    i32 = dict(dtype=torch.int32, device=dev)
+    kv_idx = torch.empty((B, H, nqb, nkb), **i32)
+    kv_cnt = torch.empty((B, H, nqb), **i32)
+    o, o_lo = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
+    mws = torch.empty(spa.mask_workspace_bytes(q.shape, w.blk_q, w.blk_k), dtype=torch.uint8,
+                      device=dev)
+    bws = torch.empty(spa.bwd_workspace_bytes(q.shape, w.blk_q, w.blk_k), dtype=torch.uint8,
+                      device=dev)
+    stream = torch.cuda.current_stream(dev)
+    stage_names = ["mask_pool", "mask_select", "fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
+
+    def step(events=None, k_frac=w.k_frac, p=w.p):
+        def mark(idx):
+            if events is not None:
+                events[idx].record(stream)
+        mark(0)
+        spa.build_mask(q, k, w.blk_q, w.blk_k, k_frac, p, out=(kv_idx, kv_cnt, None),
+                       workspace=mws, stages=spa.MASK_POOL)
+        mark(1)
+        spa.build_mask(q, k, w.blk_q, w.blk_k, k_frac, p, out=(kv_idx, kv_cnt, None),
+                       workspace=mws, stages=spa.MASK_SELECT)
+        mark(2)
+        spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k, with_residual=True,
+                            out=(o, lse, o_lo))
+        mark(3)
+        for st, idx in ((spa.BWD_PREP, 4), (spa.BWD_DKDV, 5), (spa.BWD_DQ, 6)):
+            spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k, o_lo=o_lo,
+                                out=(dq, dk, dv), workspace=bws, stages=st)
+            mark(idx)
+
+    # ---- warmup + timed steps -------------------------------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1])
+                                     for s in range(args.steps)]))
+                for i, name in enumerate(stage_names)}
+    event_step_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][6]) for s in range(args.steps)]))
+    log(f"[bench] {ms_per_step:.3f} ms/step (events {event_step_ms:.3f}); stages {stage_ms}")
+
+    # ---- algorithmic work ---------------------------------------------------------------
+    idx_h, cnt_h = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    nm = kept_pairs_weight(idx_h, cnt_h, N, w.blk_q, w.blk_k)
+    density = float(cnt_h.mean() / nkb)
+    fl_fwd, fl_dkdv, fl_dq = 4.0 * d * nm, 8.0 * d * nm, 2.0 * d * nm
+    fl_total = fl_fwd + fl_dkdv + fl_dq
+    mask_bytes = 2.0 * B * H * N * d * 2 + 4.0 * (cnt_h.sum() + B * H * nqb)
+    pool_bytes = 2.0 * B * H * N * d * 2
+    work = {
+        "mask_pool": ("hbm", pool_bytes / 1e9, "GB/s", PEAK_HBM_GBS),
+        "fwd": ("mfma", fl_fwd / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "bwd_dkdv": ("mfma", fl_dkdv / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "bwd_dq": ("mfma", fl_dq / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+    }
+    dom = max(work, key=lambda n: stage_ms[n])
+    bound, units_per_launch, unit, peak = work[dom]
+    achieved = units_per_launch / (stage_ms[dom] * 1e-3)
+    roofline = {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": None}
+    attn_ms = stage_ms["fwd"] + stage_ms["bwd_prep"] + stage_ms["bwd_dkdv"] + stage_ms["bwd_dq"]
+    mask_ms = stage_ms["mask_pool"] + stage_ms["mask_select"]
+
+    # ---- dense-mask run on the same kernels ---------------------------------------------
+    dense = None
+    if args.dense_steps > 0:
+        step(k_frac=1.0, p=1.0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.dense_steps):
+            step(k_frac=1.0, p=1.0)
+        torch.cuda.synchronize()
+        dense_ms = (time.perf_counter() - t0) * 1e3 / args.dense_steps
+        nm_dense = kept_pairs_weight(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), N, w.blk_q,
+                                     w.blk_k)
+        dense = {"ms_per_step": dense_ms, "sparse_over_dense_speedup": dense_ms / ms_per_step,
+                 "credited_tflops": 14.0 * d * nm_dense / (dense_ms * 1e-3) / 1e12}
+        log(f"[bench] dense mask: {dense_ms:.3f} ms/step")
+        step()  # restore the sparse lists
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a sample")
+        lists = {(b, h): [idx_h[b, h, i, :cnt_h[b, h, i]].astype(np.int64) for i in range(nqb)]
+                 for b in range(B) for h in range(H)}
+        cpu = cpu_oracle_baseline(g, w, lists, args.cpu_budget)
+        log(f"[bench] cpu oracle: {cpu['value']:.1f} ms/layer on {cpu['cores']} threads")
+    out = {
+        "metric": METRIC, "value": ms_per_step, "unit": "ms/layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded video-grid Q/K/V/dO, bf16)",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "blk_q": w.blk_q,
+                   "blk_k": w.blk_k, "k_frac": w.k_frac, "p": w.p, "alpha": w.alpha,
+                   "grid": list(w.grid) if w.grid else None, "density": density,
+                   "grad_dtype": "fp32"},
+        "stage_ms": stage_ms, "mask_ms": mask_ms, "attn_fwd_bwd_ms": attn_ms,
+        "credited_tflops_fwd_bwd": fl_total / (attn_ms * 1e-3) / 1e12,
+        "mfma_util_credited": fl_total / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "mask_hbm_frac": mask_bytes / (mask_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "roofline": roofline, "dense": dense, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,451 @@
+// Block-sparse attention backward over the kept tiles only, mask held fixed (abstract
+// page "SpargeAttention2: Trainable Sparse Attention via Hybrid Top-k+Top-p Masking and
+// Distillation Fine-Tuning", contribution (ii); mindverse article, section "Effiziente
+// Kernel-Implementierung und Modellanpassung").
+//
+// Launch sequence (one stream):
+//   k_dsum      D_t = <dO_t, O_t> in fp32, with O = o + o_lo when the forward pass
+//               supplied its rounding residual;
+//   k_bitmap    the kept-tile bitmap, transposed: word w of query block i at [w][i];
+//   k_collists  per key block j, the ascending list of query blocks that keep j;
+//   k_dkdv      one workgroup per (b, h, key block): walks its query-block list in
+//               ascending order, recomputes S and P, accumulates dV += P^T dO and
+//               dK += dS^T Q in registers (no atomics, fixed order);
+//   k_dq        one workgroup per (b, h, query block): walks its key-block list in
+//               ascending order and accumulates dQ += dS K.
+// All products are bf16 MFMA with fp32 accumulation.  P (in dV = P^T dO) and dS (in
+// dQ = dS K and dK = dS^T Q) enter as bf16 hi + lo pairs (about 16 bits): on peaked
+// rows dS is a difference of nearly equal terms, and dV of a key that many queries
+// attend to sums thousands of products, so a single bf16 rounding of either would be
+// visible in the gradients.
+#include "attn_tiles.h"
+#include "spa_internal.h"
+
+namespace spa {
+
+// ------------------------------------------------------------------------------------
+// D = rowsum(dO * O)
+// ------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_dsum(const uint16_t* __restrict__ o,
+                                              const uint16_t* __restrict__ o_lo,
+                                              const uint16_t* __restrict__ dout, long long rows,
+                                              float* __restrict__ dsum) {
+  constexpr int CPR = D / 8;         // lanes per row
+  constexpr int RPB = 256 / CPR;     // rows per block
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / CPR;
+  const int cc = threadIdx.x % CPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + cc * 8);
+    const uint4 b = *reinterpret_cast<const uint4*>(dout + row * D + cc * 8);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+    uint32_t wl[4] = {0u, 0u, 0u, 0u};
+    if (o_lo) {
+      const uint4 c = *reinterpret_cast<const uint4*>(o_lo + row * D + cc * 8);
+      wl[0] = c.x;
+      wl[1] = c.y;
+      wl[2] = c.z;
+      wl[3] = c.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float o0 = bf16_bits_to_f32(wa[e] & 0xFFFFu) + bf16_bits_to_f32(wl[e] & 0xFFFFu);
+      const float o1 = bf16_bits_to_f32(wa[e] >> 16) + bf16_bits_to_f32(wl[e] >> 16);
+      acc = fmaf(o0, bf16_bits_to_f32(wb[e] & 0xFFFFu), acc);
+      acc = fmaf(o1, bf16_bits_to_f32(wb[e] >> 16), acc);
+    }
+  }
+#pragma unroll
+  for (int off = CPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && cc == 0) dsum[row] = acc;
+}
+
+// ------------------------------------------------------------------------------------
+// column lists
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_bitmap(const int32_t* __restrict__ kv_idx,
+                                               const int32_t* __restrict__ kv_cnt, int nqb,
+                                               int nkb, int nw, uint32_t* __restrict__ bits) {
+  __shared__ uint32_t words[64];
+  const int bh = blockIdx.y, i = blockIdx.x, t = threadIdx.x;
+  words[t] = 0u;
+  __syncthreads();
+  const size_t row = (size_t)bh * nqb + i;
+  const int cnt = kv_cnt[row];
+  const int32_t* list = kv_idx + row * nkb;
+  for (int e = t; e < cnt; e += 64) {
+    const int j = list[e];
+    if ((unsigned)j < (unsigned)nkb) atomicOr(&words[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  if (t < nw) bits[((size_t)bh * nw + t) * nqb + i] = words[t];
+}
+
+__global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ bits, int nqb,
+                                                  int nkb, int nw, int32_t* __restrict__ q_idx,
+                                                  int32_t* __restrict__ q_cnt) {
+  extern __shared__ uint32_t colw[];  // [nqb]
+  const int bh = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
+  const uint32_t* src = bits + ((size_t)bh * nw + w) * nqb;
+  for (int x = t; x < nqb; x += 256) colw[x] = src[x];
+  __syncthreads();
+  const int lane = t & 63, wv = t >> 6;
+  for (int bb = 0; bb < 8; ++bb) {
+    const int b = wv * 8 + bb;
+    const int j = w * 32 + b;
+    if (j >= nkb) break;
+    int32_t* out = q_idx + ((size_t)bh * nkb + j) * nqb;
+    int base = 0;
+    for (int i0 = 0; i0 < nqb; i0 += 64) {
+      const int i = i0 + lane;
+      const bool on = i < nqb && ((colw[min(i, nqb - 1)] >> b) & 1u);
+      const unsigned long long ball = __ballot(on);
+      const int before = __popcll(ball & ((1ull << lane) - 1ull));
+      if (on) out[base + before] = i;
+      base += __popcll(ball);
+    }
+    if (lane == 0) q_cnt[(size_t)bh * nkb + j] = base;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// dK, dV: one workgroup per key block, 4 wavefronts.  Wavefront w owns keys
+// 32*(w&1) .. +32 of the block and the 32-row query slabs of parity w>>1.
+// ------------------------------------------------------------------------------------
+template <int D, int BQ>
+__global__ __launch_bounds__(256) void k_dkdv(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dsum,
+    const int32_t* __restrict__ q_idx, const int32_t* __restrict__ q_cnt, int N, int nqb,
+    int nkb, float scale_log2, float scale, void* __restrict__ dk_out,
+    void* __restrict__ dv_out, int grad_bf16) {
+  constexpr int LDP = TileCfg<D>::LDP;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int SLABS = BQ / 32;                 // 32-row query slabs per block
+  constexpr int QCH = BQ * D / 8;                // 16-byte chunks of one [BQ, D] tile
+  constexpr int NCH = QCH / 256;
+  constexpr int STAGE = 2 * BQ * LDP * 2 + 2 * BQ * 4;    // Q, dO tiles + lse2, dsum
+  constexpr int RED = 2 * 2 * 64 * DB * 16 * 4;           // reduction of dK, dV partials
+  constexpr int SMEM = STAGE > RED ? STAGE : RED;
+  __shared__ __align__(16) unsigned char smem[SMEM];
+  uint16_t* Qs = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* dOs = Qs + BQ * LDP;
+  float* lse2s = reinterpret_cast<float*>(dOs + BQ * LDP);
+  float* dss = lse2s + BQ;
+
+  const int bh = blockIdx.y, j = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  const int kh = wv & 1, par = wv >> 1;
+  const size_t head = (size_t)bh * N * D;
+  const int key = j * kBlkK + 32 * kh + c;  // this lane's key (B operand column)
+  const bool kvalid = key < N;
+
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    if (kvalid) {
+      kf[kk] = *reinterpret_cast<const bf16x8*>(k + head + (size_t)key * D + 16 * kk + 8 * h);
+      vf[kk] = *reinterpret_cast<const bf16x8*>(v + head + (size_t)key * D + 16 * kk + 8 * h);
+    } else {
+      kf[kk] = bf16x8{};
+      vf[kk] = bf16x8{};
+    }
+  }
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+
+  const int32_t* list = q_idx + ((size_t)bh * nkb + j) * nqb;
+  const int cnt = q_cnt[(size_t)bh * nkb + j];
+  for (int it = 0; it < cnt; ++it) {
+    const int i = list[it];
+    const int row0 = i * BQ;
+    {  // stage Q_i, dO_i, lse, D
+      uint4 qr[NCH], dr[NCH];
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        const int x = t + 256 * u;
+        const int row = x / (D / 8), cc = x % (D / 8);
+        const int grow = row0 + row;
+        const bool ok = grow < N;
+        qr[u] = ok ? *reinterpret_cast<const uint4*>(q + head + (size_t)grow * D + cc * 8)
+                   : make_uint4(0, 0, 0, 0);
+        dr[u] = ok ? *reinterpret_cast<const uint4*>(dout + head + (size_t)grow * D + cc * 8)
+                   : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        const int x = t + 256 * u;
+        const int row = x / (D / 8), cc = x % (D / 8);
+        *reinterpret_cast<uint4*>(Qs + row * LDP + cc * 8) = qr[u];
+        *reinterpret_cast<uint4*>(dOs + row * LDP + cc * 8) = dr[u];
+      }
+      if (t < BQ) {
+        const int grow = row0 + t;
+        const bool ok = grow < N;
+        lse2s[t] = ok ? lse[(size_t)bh * N + grow] * kLog2e : INFINITY;
+        dss[t] = ok ? dsum[(size_t)bh * N + grow] : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sl = par; sl < SLABS; sl += 2) {
+      const int r0 = 32 * sl;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        s = mfma32(lds_rowfrag<D>(Qs, r0, kk, lane), kf[kk], s);
+        dp = mfma32(lds_rowfrag<D>(dOs, r0, kk, lane), vf[kk], dp);
+      }
+      // element e: query r0 + acc_row(e, h), key = this lane's key
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int qr_ = r0 + acc_row(e, h);
+        const float pe = kvalid ? __builtin_amdgcn_exp2f(s[e] * scale_log2 - lse2s[qr_]) : 0.f;
+        s[e] = pe;
+        dp[e] = pe * (dp[e] - dss[qr_]);
+      }
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        bf16x8 ph, pl, dh, dl;
+        split_bf16x8(s, kq, ph, pl);
+        split_bf16x8(dp, kq, dh, dl);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 ob = lds_colfrag<D>(dOs, r0 + 16 * kq, 32 * db, lane);
+          dva[db] = mfma32(ph, ob, dva[db]);
+          dva[db] = mfma32(pl, ob, dva[db]);
+          const bf16x8 qb = lds_colfrag<D>(Qs, r0 + 16 * kq, 32 * db, lane);
+          dka[db] = mfma32(dh, qb, dka[db]);
+          dka[db] = mfma32(dl, qb, dka[db]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- reduce the two query-slab parities and write -----------------------------------
+  float* red = reinterpret_cast<float*>(smem);  // [kh][K|V][lane][DB*16]
+  if (par == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        red[((kh * 2 + 0) * 64 + lane) * (DB * 16) + db * 16 + e] = dka[db][e];
+        red[((kh * 2 + 1) * 64 + lane) * (DB * 16) + db * 16 + e] = dva[db][e];
+      }
+  }
+  __syncthreads();
+  if (par == 0) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float gk = (dka[db][e] + red[((kh * 2 + 0) * 64 + lane) * (DB * 16) + db * 16 + e]) * scale;
+        const float gv = dva[db][e] + red[((kh * 2 + 1) * 64 + lane) * (DB * 16) + db * 16 + e];
+        // accumulator element e: key row 8*(e/4) + 4*h + e%4 of this wave's 32 keys, column c
+        const int krow = j * kBlkK + 32 * kh + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (krow < N) {
+          const size_t off = head + (size_t)krow * D + 32 * db + c;
+          if (grad_bf16) {
+            reinterpret_cast<uint16_t*>(dk_out)[off] = (uint16_t)f32_to_bf16_bits(gk);
+            reinterpret_cast<uint16_t*>(dv_out)[off] = (uint16_t)f32_to_bf16_bits(gv);
+          } else {
+            reinterpret_cast<float*>(dk_out)[off] = gk;
+            reinterpret_cast<float*>(dv_out)[off] = gv;
+          }
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// dQ: one workgroup per query block, one wavefront per 32 query rows.
+// ------------------------------------------------------------------------------------
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2) void k_dq(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dsum,
+    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int N, int nqb,
+    int nkb, float scale_log2, float scale, void* __restrict__ dq_out, int grad_bf16) {
+  constexpr int NT = BQ * 2;
+  constexpr int NCH = TileCfg<D>::CHUNKS / NT;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  __shared__ __align__(16) uint16_t smem[2][2][TileCfg<D>::TILE];  // [buf][K|V]
+
+  const int bh = blockIdx.y, i = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  const size_t head = (size_t)bh * N * D;
+  const uint16_t* kh_ = k + head;
+  const uint16_t* vh_ = v + head;
+  const int32_t* list = kv_idx + ((size_t)bh * nqb + i) * nkb;
+  const int cnt = kv_cnt[(size_t)bh * nqb + i];
+
+  const int qrow = i * BQ + 32 * wv + c;
+  const bool qvalid = qrow < N;
+  bf16x8 qf[KS], df[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    if (qvalid) {
+      qf[kk] = *reinterpret_cast<const bf16x8*>(q + head + (size_t)qrow * D + 16 * kk + 8 * h);
+      df[kk] = *reinterpret_cast<const bf16x8*>(dout + head + (size_t)qrow * D + 16 * kk + 8 * h);
+    } else {
+      qf[kk] = bf16x8{};
+      df[kk] = bf16x8{};
+    }
+  }
+  const float lse2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : INFINITY;
+  const float dq_sum = qvalid ? dsum[(size_t)bh * N + qrow] : 0.f;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  uint4 kr[NCH], vr[NCH];
+  if (cnt > 0) {
+    const int j0 = list[0];
+    tile_load<D, NT>(kr, kh_, j0 * kBlkK, N);
+    tile_load<D, NT>(vr, vh_, j0 * kBlkK, N);
+    tile_store<D, NT>(kr, smem[0][0]);
+    tile_store<D, NT>(vr, smem[0][1]);
+  }
+  __syncthreads();
+  for (int t = 0; t < cnt; ++t) {
+    const int buf = t & 1;
+    const int j = list[t];
+    if (t + 1 < cnt) {
+      const int jn = list[t + 1];
+      tile_load<D, NT>(kr, kh_, jn * kBlkK, N);
+      tile_load<D, NT>(vr, vh_, jn * kBlkK, N);
+    }
+    const uint16_t* Ks = smem[buf][0];
+    const uint16_t* Vs = smem[buf][1];
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        s[kb] = mfma32(lds_rowfrag<D>(Ks, 32 * kb, kk, lane), qf[kk], s[kb]);
+        dp[kb] = mfma32(lds_rowfrag<D>(Vs, 32 * kb, kk, lane), df[kk], dp[kb]);
+      }
+    }
+    const int key0 = j * kBlkK;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const bool ok = key0 + 32 * kb + acc_row(e, h) < N;
+        const float pe = ok ? __builtin_amdgcn_exp2f(s[kb][e] * scale_log2 - lse2) : 0.f;
+        dp[kb][e] = pe * (dp[kb][e] - dq_sum);
+      }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 dh, dl;
+      split_bf16x8(dp[kk >> 1], kk & 1, dh, dl);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 ka = lds_colfrag<D>(Ks, 16 * kk, 32 * db, lane);
+        acc[db] = mfma32(ka, dh, acc[db]);
+        acc[db] = mfma32(ka, dl, acc[db]);
+      }
+    }
+    if (t + 1 < cnt) {
+      tile_store<D, NT>(kr, smem[buf ^ 1][0]);
+      tile_store<D, NT>(vr, smem[buf ^ 1][1]);
+    }
+    __syncthreads();
+  }
+  if (qvalid) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * h;
+        const size_t off = head + (size_t)qrow * D + d0;
+        const float x0 = acc[db][4 * g + 0] * scale, x1 = acc[db][4 * g + 1] * scale;
+        const float x2 = acc[db][4 * g + 2] * scale, x3 = acc[db][4 * g + 3] * scale;
+        if (grad_bf16) {
+          uint2 pk;
+          pk.x = pack_bf16x2(x0, x1);
+          pk.y = pack_bf16x2(x2, x3);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dq_out) + off) = pk;
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(dq_out) + off) =
+              make_float4(x0, x1, x2, x3);
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// host side
+// ------------------------------------------------------------------------------------
+static int n_words(const Geometry& g) { return (g.nkb + 31) / 32; }
+
+size_t bwd_workspace_bytes(const Geometry& g) {
+  const size_t bh = (size_t)g.bh();
+  return align_up(bh * g.N * sizeof(float), 256) +
+         align_up(bh * n_words(g) * g.nqb * sizeof(uint32_t), 256) +
+         align_up(bh * g.nkb * g.nqb * sizeof(int32_t), 256) +
+         align_up(bh * g.nkb * sizeof(int32_t), 256);
+}
+
+void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a) {
+  const size_t bh = (size_t)g.bh();
+  char* p = static_cast<char*>(ws);
+  a->dsum = reinterpret_cast<float*>(p);
+  p += align_up(bh * g.N * sizeof(float), 256);
+  a->bits = reinterpret_cast<uint32_t*>(p);
+  p += align_up(bh * n_words(g) * g.nqb * sizeof(uint32_t), 256);
+  a->q_idx = reinterpret_cast<int32_t*>(p);
+  p += align_up(bh * g.nkb * g.nqb * sizeof(int32_t), 256);
+  a->q_cnt = reinterpret_cast<int32_t*>(p);
+}
+
+template <int D, int BQ>
+static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s) {
+  const Geometry& g = a.g;
+  const float sl2 = a.scale * kLog2e;
+  if (stages & 1u) {
+    const long long rows = (long long)g.bh() * g.N;
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((k_dsum<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s,
+                       a.o, a.o_lo, a.dout, rows, a.dsum);
+    const int nw = n_words(g);
+    hipLaunchKernelGGL(k_bitmap, dim3(g.nqb, (unsigned)g.bh()), dim3(64), 0, s, a.kv_idx,
+                       a.kv_cnt, g.nqb, g.nkb, nw, a.bits);
+    hipLaunchKernelGGL(k_collists, dim3(nw, (unsigned)g.bh()), dim3(256),
+                       g.nqb * sizeof(uint32_t), s, a.bits, g.nqb, g.nkb, nw, a.q_idx, a.q_cnt);
+  }
+  if (stages & 2u)
+    hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(g.nkb, (unsigned)g.bh()), dim3(256), 0, s, a.q, a.k,
+                       a.v, a.dout, a.lse, a.dsum, a.q_idx, a.q_cnt, g.N, g.nqb, g.nkb, sl2,
+                       a.scale, a.dk, a.dv, a.grad_bf16);
+  if (stages & 4u)
+    hipLaunchKernelGGL((k_dq<D, BQ>), dim3(g.nqb, (unsigned)g.bh()), dim3(BQ * 2), 0, s, a.q, a.k,
+                       a.v, a.dout, a.lse, a.dsum, a.kv_idx, a.kv_cnt, g.N, g.nqb, g.nkb, sl2,
+                       a.scale, a.dq, a.grad_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, unsigned stages, hipStream_t s) {
+  const int d = a.g.d, bq = a.g.blk_q;
+  if (d == 128 && bq == 128) return launch_bwd_t<128, 128>(a, stages, s);
+  if (d == 128 && bq == 64) return launch_bwd_t<128, 64>(a, stages, s);
+  if (d == 64 && bq == 128) return launch_bwd_t<64, 128>(a, stages, s);
+  return launch_bwd_t<64, 64>(a, stages, s);
+}
+
+}  // namespace spa

@@ -1,0 +1,81 @@
+// Internal launch interface between the C ABI (spa_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spa {
+
+struct Geometry {
+  int B, H, N, d, blk_q, blk_k;
+  int nqb, nkb;  // ceil(N / blk_q), ceil(N / blk_k)
+  long long bh() const { return (long long)B * H; }
+};
+
+// ---- mask ----------------------------------------------------------------------------
+struct MaskArgs {
+  Geometry g;
+  const uint16_t* q;
+  const uint16_t* k;
+  double pooled_scale;
+  int lk;             // Top-k length, already clamped to [1, nkb]
+  int p_all;          // p >= 1: keep every block
+  uint64_t wp;        // Top-p target mass in units of 2^-62
+  int32_t* kv_idx;
+  int32_t* kv_cnt;
+  int32_t* rule_len;  // may be null
+  double* qbar;       // workspace [BH][nqb][d]
+  double* kbar_t;     // workspace [BH][d][nkb]
+};
+size_t mask_workspace_bytes(const Geometry& g);
+void mask_workspace_carve(const Geometry& g, void* ws, double** qbar, double** kbar_t);
+// stage bits: 1 = pooling, 2 = selection
+hipError_t launch_mask(const MaskArgs& a, unsigned stages, hipStream_t s);
+
+// ---- forward ------------------------------------------------------------------------
+struct FwdArgs {
+  Geometry g;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* kv_idx;
+  const int32_t* kv_cnt;
+  float scale;
+  uint16_t* o;
+  uint16_t* o_lo;  // may be null
+  float* lse;
+};
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
+
+// ---- backward -----------------------------------------------------------------------
+struct BwdArgs {
+  Geometry g;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* o_lo;  // may be null
+  const uint16_t* dout;
+  const float* lse;
+  const int32_t* kv_idx;
+  const int32_t* kv_cnt;
+  float scale;
+  void* dq;
+  void* dk;
+  void* dv;
+  int grad_bf16;
+  // workspace sections
+  float* dsum;      // [BH][N]
+  uint32_t* bits;   // [BH][ceil(nkb/32)][nqb]
+  int32_t* q_idx;   // [BH][nkb][nqb]
+  int32_t* q_cnt;   // [BH][nkb]
+};
+size_t bwd_workspace_bytes(const Geometry& g);
+void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a);
+// stage bits: 1 = D and the column lists, 2 = dK/dV, 4 = dQ
+hipError_t launch_bwd(const BwdArgs& a, unsigned stages, hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace spa

@@ -1,0 +1,132 @@
+"""GPU parity at the full Wan2.1-1.3B-480p layer shape (B=1, H=12, N=32760, d=128,
+blocks 128 x 64, k=5 %, p=0.9), in the launch configuration the benchmark times.
+
+The mask is compared on every row.  O, LSE and dQ are compared on sampled query blocks
+(every row of each), dK and dV on sampled key blocks (every query block that keeps them
+contributes), and invariants that hold at any size are checked on the whole tensors.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_pooled_amd as spa
+from block_sparse_attention_pooled_amd import synth
+from oracle import spa_oracle as O
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS["wan13b_480p"]
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def c2():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    log(f"[fullsize] generating {W.name} {W.shape()}")
+    g = synth.generate(W)
+    dev = {n: torch.from_numpy(g[n].view(np.int16)).view(torch.bfloat16).cuda() for n in g}
+
+    def run():
+        kv_idx, kv_cnt, rl = spa.build_mask(dev["q"], dev["k"], W.blk_q, W.blk_k, W.k_frac, W.p,
+                                            rule_len=True)
+        o, lse, o_lo = spa.sparse_attn_fwd(dev["q"], dev["k"], dev["v"], kv_idx, kv_cnt, W.blk_q,
+                                           W.blk_k, with_residual=True)
+        dq, dk, dv = spa.sparse_attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, kv_idx,
+                                         kv_cnt, W.blk_q, W.blk_k, o_lo=o_lo)
+        torch.cuda.synchronize()
+        return dict(kv_idx=kv_idx, kv_cnt=kv_cnt, rule_len=rl, o=o, o_lo=o_lo, lse=lse, dq=dq,
+                    dk=dk, dv=dv)
+
+    log("[fullsize] GPU run")
+    res = run()
+    host = {k: (v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy())
+            for k, v in res.items()}
+    f64 = {n: O.widen_bf16(g[n]) for n in g}
+    return dict(torch=torch, g=g, dev=dev, run=run, res=res, host=host, f64=f64)
+
+
+def test_fullsize_mask_all_rows(c2):
+    h = c2["host"]
+    log("[fullsize] oracle mask (all heads)")
+    mask = O.build_mask(c2["f64"]["q"], c2["f64"]["k"], W.blk_q, W.blk_k, W.k_frac, W.p)
+    n, exempt, fails = parity.compare_mask_rows(h["kv_idx"], h["kv_cnt"], mask["rows"], W.p)
+    dens = h["kv_cnt"].mean() / W.n_kblk
+    log(f"  {n} rows, {len(exempt)} exempt {exempt[:3]}, density={dens:.4f}")
+    assert n == W.B * W.H * W.n_qblk
+    assert not fails, fails[:5]
+    lk = O.topk_count(W.k_frac, W.n_kblk)
+    assert np.all(h["rule_len"][..., 0] == lk)
+    assert 0.04 < dens < 0.07
+
+
+def _sample_qblocks():
+    return [(0, 0, 0), (0, 3, 97), (0, 7, 200), (0, 11, W.n_qblk - 1), (0, 5, 128)]
+
+
+def test_fullsize_fwd_and_dq_sampled(c2):
+    h, f = c2["host"], c2["f64"]
+    lists = parity.lists_from_gpu(h["kv_idx"], h["kv_cnt"])
+    for (b, hh, i) in _sample_qblocks():
+        log(f"[fullsize] fwd/dQ q-block (b={b}, h={hh}, i={i})")
+        o, lse = O.sparse_attn_fwd(f["q"], f["k"], f["v"], lists, W.blk_q, W.blk_k,
+                                   heads=[(b, hh)], qblocks=[i])
+        s, e = i * W.blk_q, min(W.N, (i + 1) * W.blk_q)
+        for name, got, want in (("O", h["o"][b, hh, s:e], o[b, hh, s:e]),
+                                ("LSE", h["lse"][b, hh, s:e], lse[b, hh, s:e])):
+            ok, mx, rel, _ = parity.close(got, want)
+            log(f"  {name}: max_abs={mx:.3e} rel_l2={rel:.3e}")
+            assert ok, (name, mx, rel)
+        dq, _, _ = O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, W.blk_q, W.blk_k,
+                                     heads=[(b, hh)], qblocks=[i])
+        ok, mx, rel, _ = parity.close(h["dq"][b, hh, s:e], dq[b, hh, s:e])
+        log(f"  dQ: max_abs={mx:.3e} rel_l2={rel:.3e}")
+        assert ok, ("dQ", mx, rel)
+
+
+def test_fullsize_dkdv_sampled(c2):
+    h, f = c2["host"], c2["f64"]
+    lists = parity.lists_from_gpu(h["kv_idx"], h["kv_cnt"])
+    for (b, hh, j) in [(0, 0, 0), (0, 4, 255), (0, 11, W.n_kblk - 1), (0, 8, 301)]:
+        users = [i for i, keep in enumerate(lists[(b, hh)]) if j in set(keep.tolist())]
+        log(f"[fullsize] dK/dV key block (b={b}, h={hh}, j={j}) kept by {len(users)} query blocks")
+        _, dk, dv = O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, W.blk_q, W.blk_k,
+                                      heads=[(b, hh)], qblocks=users)
+        s, e = j * W.blk_k, min(W.N, (j + 1) * W.blk_k)
+        for name, got, want in (("dK", h["dk"][b, hh, s:e], dk[b, hh, s:e]),
+                                ("dV", h["dv"][b, hh, s:e], dv[b, hh, s:e])):
+            ok, mx, rel, _ = parity.close(got, want)
+            log(f"  {name}: max_abs={mx:.3e} rel_l2={rel:.3e}")
+            assert ok, (name, mx, rel)
+
+
+def test_fullsize_gradient_invariants(c2):
+    h, f = c2["host"], c2["f64"]
+    for hh in range(W.H):
+        dk, dv, dq = (h[n][0, hh].astype(np.float64) for n in ("dk", "dv", "dq"))
+        q, k, do = f["q"][0, hh], f["k"][0, hh], f["do"][0, hh]
+        # softmax shift invariance: the key gradients of each query row sum to zero
+        assert np.abs(dk.sum(axis=0)).max() <= 1e-3 * np.abs(dk).sum(axis=0).max()
+        np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=0.05)
+        qdq, kdk = float(np.sum(q * dq)), float(np.sum(k * dk))
+        assert abs(qdq - kdk) <= 1e-3 * (np.abs(q * dq).sum() + np.abs(k * dk).sum())
+
+
+def test_fullsize_deterministic(c2):
+    torch = c2["torch"]
+    again = c2["run"]()
+    for name, t in c2["res"].items():
+        if name == "kv_idx":  # only the first kv_cnt entries of a row are defined
+            a, b = t.cpu().numpy(), again[name].cpu().numpy()
+            cnt = c2["host"]["kv_cnt"]
+            for (bb, hh, i), c in np.ndenumerate(cnt):
+                assert np.array_equal(a[bb, hh, i, :c], b[bb, hh, i, :c]), (bb, hh, i)
+            continue
+        assert torch.equal(t, again[name]), name

@@ -1,0 +1,146 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 CPU oracle.
+
+Mask: kept lists bit-exact except blocks within 1e-6 of the row threshold (reported).
+Attention: O, LSE, dQ, dK, dV computed with the GPU's mask, max-abs <= 2e-2 and
+relative L2 <= 1e-2.
+"""
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_pooled_amd as spa
+from block_sparse_attention_pooled_amd import synth
+from oracle import spa_oracle as O
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    spa.load_library()
+    return torch
+
+
+def to_dev(torch, bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(torch, g, w, k_frac, p, with_bwd=True):
+    q, k, v = (to_dev(torch, g[n]) for n in ("q", "k", "v"))
+    kv_idx, kv_cnt, rl = spa.build_mask(q, k, w.blk_q, w.blk_k, k_frac, p, rule_len=True)
+    o, lse, o_lo = spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                                       with_residual=True)
+    o_plain, lse_plain = spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k)
+    res = dict(kv_idx=kv_idx.cpu().numpy(), kv_cnt=kv_cnt.cpu().numpy(), rule_len=rl.cpu().numpy(),
+               o=o.float().cpu().numpy(), lse=lse.cpu().numpy(),
+               o_full=(o.float() + o_lo.float()).cpu().numpy(),
+               o_plain=o_plain.float().cpu().numpy(), lse_plain=lse_plain.cpu().numpy())
+    if with_bwd:
+        do = to_dev(torch, g["do"])
+        dq, dk, dv = spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                                         o_lo=o_lo)
+        res.update(dq=dq.cpu().numpy(), dk=dk.cpu().numpy(), dv=dv.cpu().numpy())
+    torch.cuda.synchronize()
+    return res
+
+
+def check_close(name, got, want):
+    ok, mx, rel, scaled = parity.close(got, want)
+    log(f"  {name}: max_abs={mx:.3e} rel_l2={rel:.3e} max_abs/max(1,|x|inf)={scaled:.3e}")
+    assert ok, f"{name}: max_abs={mx:.3e} rel_l2={rel:.3e} scaled={scaled:.3e}"
+
+
+def small_workload(N, d, bq, grid=None, kind="video", seed=3, B=1, H=2):
+    if grid is None:
+        kind = "tiny"
+    return synth.Workload(f"small_{N}_{d}_{bq}", B, H, N, d, bq, 64, 0.1, 0.9, kind=kind,
+                          grid=grid, alpha=synth.ALPHA_480P, n_sinks=2, seed=seed)
+
+
+SMALL = [
+    ("tiny", synth.WORKLOADS["tiny"]),
+    ("tiny_sparse", synth.WORKLOADS["tiny_sparse"]),
+    ("n1000_d128_q128", small_workload(1000, 128, 128, grid=(2, 20, 25), B=2, H=3)),
+    ("n1000_d128_q64", small_workload(1000, 128, 64, grid=(2, 20, 25))),
+    ("n1000_d64_q128", small_workload(1000, 64, 128, grid=(2, 20, 25))),
+    ("n777_d64_q64", small_workload(777, 64, 64, grid=(3, 7, 37))),
+    ("n65_d128_q128", small_workload(65, 128, 128)),
+    ("n50_d64_q64", small_workload(50, 64, 64)),
+]
+
+
+def full_check(torch, w, k_frac, p, tag):
+    log(f"[case {tag}] shape={w.shape()} blk=({w.blk_q},{w.blk_k}) k={k_frac} p={p}")
+    g = synth.generate(w)
+    res = run_gpu(torch, g, w, k_frac, p)
+    q, k, v, do = (O.widen_bf16(g[n]) for n in ("q", "k", "v", "do"))
+    mask = O.build_mask(q, k, w.blk_q, w.blk_k, k_frac, p)
+    n, exempt, fails = parity.compare_mask_rows(res["kv_idx"], res["kv_cnt"], mask["rows"], p)
+    log(f"  mask: {n} rows, {len(exempt)} exempt near-threshold rows {exempt[:5]}")
+    assert not fails, fails[:5]
+    for (b, h), rows in mask["rows"].items():
+        for i, r in enumerate(rows):
+            assert res["rule_len"][b, h, i, 0] == r["Lk"]
+            if not exempt:
+                assert res["rule_len"][b, h, i, 1] == r["Lp"], (b, h, i)
+    lists = parity.lists_from_gpu(res["kv_idx"], res["kv_cnt"])
+    o, lse = O.sparse_attn_fwd(q, k, v, lists, w.blk_q, w.blk_k)
+    check_close("O", res["o"], o)
+    check_close("O without residual", res["o_plain"], o)
+    check_close("LSE", res["lse"], lse)
+    assert np.array_equal(res["lse"], res["lse_plain"])
+    # o + o_lo carries O to ~16 bits
+    ok_full, mx_full, _, _ = parity.close(res["o_full"], o, atol=2e-4, rtol_l2=1e-4)
+    log(f"  O + o_lo: max_abs={mx_full:.3e}")
+    assert ok_full
+    dq, dk, dv = O.sparse_attn_bwd(q, k, v, do, lists, w.blk_q, w.blk_k)
+    check_close("dQ", res["dq"], dq)
+    check_close("dK", res["dk"], dk)
+    check_close("dV", res["dv"], dv)
+
+
+@pytest.mark.parametrize("tag,w", SMALL, ids=[s[0] for s in SMALL])
+def test_small_parity(torch_gpu, tag, w):
+    full_check(torch_gpu, w, w.k_frac, w.p, tag)
+
+
+RULES = [(0.1, 0.9), (0.0, 0.7), (0.2, 0.0), (1.0, 0.5), (0.05, 1.0), (0.0, 0.0), (0.3, 0.95)]
+
+
+@pytest.mark.parametrize("k_frac,p", RULES)
+def test_rule_variants_parity(torch_gpu, k_frac, p):
+    w = small_workload(1000, 128, 128, grid=(2, 20, 25))
+    full_check(torch_gpu, w, k_frac, p, f"rules k={k_frac} p={p}")
+
+
+def test_stress_rows_parity(torch_gpu):
+    # near-uniform and sink-dominated heads at reduced length
+    w = dataclasses.replace(synth.WORKLOADS["stress"], N=4000, grid=(4, 20, 50), H=4)
+    for k_frac, p in ((0.02, 0.7), (0.05, 0.9), (0.1, 0.95)):
+        full_check(torch_gpu, w, k_frac, p, f"stress k={k_frac} p={p}")
+
+
+def test_determinism(torch_gpu):
+    torch = torch_gpu
+    w = small_workload(1000, 128, 128, grid=(2, 20, 25), B=2, H=3)
+    g = synth.generate(w)
+    a = run_gpu(torch, g, w, 0.1, 0.9)
+    b = run_gpu(torch, g, w, 0.1, 0.9)
+    assert np.array_equal(a["kv_cnt"], b["kv_cnt"])
+    for (bb, hh, i), c in np.ndenumerate(a["kv_cnt"]):  # defined prefix of each list
+        assert np.array_equal(a["kv_idx"][bb, hh, i, :c], b["kv_idx"][bb, hh, i, :c])
+    for key in a:
+        if key != "kv_idx":
+            assert np.array_equal(a[key], b[key], equal_nan=True), key
