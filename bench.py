@@ -68,10 +68,11 @@ def cpu_oracle_baseline(g, w, lists, budget_s: float):
              for x in range(len(heads) * w.n_qblk)]
     done = 0
     t0 = time.perf_counter()
-    for (bh, i) in order:
-        O.sparse_attn_fwd(f["q"], f["k"], f["v"], lists, w.blk_q, w.blk_k, heads=[bh],
-                          qblocks=[i])
-        O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, w.blk_q, w.blk_k, heads=[bh],
+    for ((b, h), i) in order:
+        one = {n: f[n][b:b + 1, h:h + 1] for n in f}   # this head only
+        l1 = {(0, 0): lists[(b, h)]}
+        O.sparse_attn_fwd(one["q"], one["k"], one["v"], l1, w.blk_q, w.blk_k, qblocks=[i])
+        O.sparse_attn_bwd(one["q"], one["k"], one["v"], one["do"], l1, w.blk_q, w.blk_k,
                           qblocks=[i])
         done += 1
         if time.perf_counter() - t0 > budget_s:
