@@ -46,7 +46,7 @@ class _Dims(ctypes.Structure):
 
 
 def library_path() -> str:
-    return os.environ.get("SPA_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+    return os.environ.get("SPA_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
 
 
 def load_library():

@@ -16,6 +16,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep small private arrays (staging registers) in VGPRs: promoting them to LDS would
+    # take LDS that the tiles need and cost a workgroup of occupancy
+    "-mllvm", "-disable-promote-alloca-to-lds=true",
     "-I" + os.path.join(ROOT, "include"), "-Wno-unused-result",
 ]
 

@@ -110,8 +110,11 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
 }
 
 // ------------------------------------------------------------------------------------
-// dK, dV: one workgroup per key block, 4 wavefronts.  Wavefront w owns keys
-// 32*(w&1) .. +32 of the block and the 32-row query slabs of parity w>>1.
+// dK, dV: one workgroup per key block (workgroups in XCD-contiguous order), 4 wavefronts.
+// The key block's query-block list is walked in 64-row stages (a 128-row query block is
+// two stages); Q and dO of the next stage are loaded while the current one is used.
+// Wavefront w owns keys 32*(w&1) .. +32 of the block and the 32-row slab w>>1 of each
+// stage; the two slab parities are summed at the end in a fixed order.
 // ------------------------------------------------------------------------------------
 template <int D, int BQ>
 __global__ __launch_bounds__(256) void k_dkdv(
@@ -119,24 +122,24 @@ __global__ __launch_bounds__(256) void k_dkdv(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum,
     const int32_t* __restrict__ q_idx, const int32_t* __restrict__ q_cnt, int N, int nqb,
-    int nkb, float scale_log2, float scale, void* __restrict__ dk_out,
+    int nkb, int total, float scale_log2, float scale, void* __restrict__ dk_out,
     void* __restrict__ dv_out, int grad_bf16) {
-  constexpr int LDP = TileCfg<D>::LDP;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int SLABS = BQ / 32;                 // 32-row query slabs per block
-  constexpr int QCH = BQ * D / 8;                // 16-byte chunks of one [BQ, D] tile
-  constexpr int NCH = QCH / 256;
-  constexpr int STAGE = 2 * BQ * LDP * 2 + 2 * BQ * 4;    // Q, dO tiles + lse2, dsum
-  constexpr int RED = 2 * 2 * 64 * DB * 16 * 4;           // reduction of dK, dV partials
-  constexpr int SMEM = STAGE > RED ? STAGE : RED;
+  constexpr int STG = 64;                 // query rows per stage
+  constexpr int SPB = BQ / STG;           // stages per query block
+  constexpr int TILE = STG * D;           // elements of one staged Q or dO tile
+  constexpr int STAGE_BYTES = 2 * (2 * TILE * 2 + 2 * STG * 4);  // 2 buffers: Q, dO, lse2, D
+  constexpr int RED_BYTES = 2 * 2 * 64 * DB * 16 * 4;            // dK, dV partials
+  constexpr int SMEM = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
   __shared__ __align__(16) unsigned char smem[SMEM];
-  uint16_t* Qs = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* dOs = Qs + BQ * LDP;
-  float* lse2s = reinterpret_cast<float*>(dOs + BQ * LDP);
-  float* dss = lse2s + BQ;
+  auto Qs = [&](int b) { return reinterpret_cast<uint16_t*>(smem) + b * 2 * TILE; };
+  auto dOs = [&](int b) { return reinterpret_cast<uint16_t*>(smem) + b * 2 * TILE + TILE; };
+  float* side = reinterpret_cast<float*>(smem + 2 * 2 * TILE * 2);  // [buf][lse2 | D][STG]
 
-  const int bh = blockIdx.y, j = blockIdx.x;
+  const int tile_id = xcd_remap(blockIdx.x, total);
+  const int bh = tile_id / nkb;
+  const int j = tile_id - bh * nkb;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int c = lane & 31, h = lane >> 5;
   const int kh = wv & 1, par = wv >> 1;
@@ -145,14 +148,12 @@ __global__ __launch_bounds__(256) void k_dkdv(
   const bool kvalid = key < N;
 
   bf16x8 kf[KS], vf[KS];
+  {
+    const size_t krow = head + (size_t)min(key, N - 1) * D + 8 * h;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    if (kvalid) {
-      kf[kk] = *reinterpret_cast<const bf16x8*>(k + head + (size_t)key * D + 16 * kk + 8 * h);
-      vf[kk] = *reinterpret_cast<const bf16x8*>(v + head + (size_t)key * D + 16 * kk + 8 * h);
-    } else {
-      kf[kk] = bf16x8{};
-      vf[kk] = bf16x8{};
+    for (int kk = 0; kk < KS; ++kk) {
+      kf[kk] = *reinterpret_cast<const bf16x8*>(k + krow + 16 * kk);
+      vf[kk] = *reinterpret_cast<const bf16x8*>(v + krow + 16 * kk);
     }
   }
   f32x16 dka[DB], dva[DB];
@@ -163,75 +164,86 @@ __global__ __launch_bounds__(256) void k_dkdv(
   }
 
   const int32_t* list = q_idx + ((size_t)bh * nkb + j) * nqb;
-  const int cnt = q_cnt[(size_t)bh * nkb + j];
-  for (int it = 0; it < cnt; ++it) {
-    const int i = list[it];
-    const int row0 = i * BQ;
-    {  // stage Q_i, dO_i, lse, D
-      uint4 qr[NCH], dr[NCH];
-#pragma unroll
-      for (int u = 0; u < NCH; ++u) {
-        const int x = t + 256 * u;
-        const int row = x / (D / 8), cc = x % (D / 8);
-        const int grow = row0 + row;
-        const bool ok = grow < N;
-        qr[u] = ok ? *reinterpret_cast<const uint4*>(q + head + (size_t)grow * D + cc * 8)
-                   : make_uint4(0, 0, 0, 0);
-        dr[u] = ok ? *reinterpret_cast<const uint4*>(dout + head + (size_t)grow * D + cc * 8)
-                   : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < NCH; ++u) {
-        const int x = t + 256 * u;
-        const int row = x / (D / 8), cc = x % (D / 8);
-        *reinterpret_cast<uint4*>(Qs + row * LDP + cc * 8) = qr[u];
-        *reinterpret_cast<uint4*>(dOs + row * LDP + cc * 8) = dr[u];
-      }
-      if (t < BQ) {
-        const int grow = row0 + t;
-        const bool ok = grow < N;
-        lse2s[t] = ok ? lse[(size_t)bh * N + grow] * kLog2e : INFINITY;
-        dss[t] = ok ? dsum[(size_t)bh * N + grow] : 0.f;
+  const int nstage = q_cnt[(size_t)bh * nkb + j] * SPB;
+  // staging of stage st: Q and dO rows [r0, r0 + 64) plus their lse2 and D values
+  Stager<D, STG, 256> qst, dst_;
+  float lse_r = 0.f, d_r = 0.f;
+  if (nstage > 0) {
+    const int r0 = list[0] * BQ;
+    qst.load(q + head, r0, N);
+    dst_.load(dout + head, r0, N);
+    if (t < STG) {
+      const int grow = r0 + t;
+      const size_t gi = (size_t)bh * N + min(grow, N - 1);
+      lse_r = grow < N ? lse[gi] * kLog2e : INFINITY;  // rows beyond N get P = 0
+      d_r = grow < N ? dsum[gi] : 0.f;
+    }
+    qst.store(Qs(0));
+    dst_.store(dOs(0));
+    if (t < STG) {
+      side[0 * STG + t] = lse_r;
+      side[1 * STG + t] = d_r;
+    }
+  }
+  __syncthreads();
+  for (int st = 0; st < nstage; ++st) {
+    const int b = st & 1;
+    {  // next stage (the last stage reloads itself; the copy goes unused)
+      const int sn = min(st + 1, nstage - 1);
+      const int r0 = list[sn / SPB] * BQ + (sn % SPB) * STG;
+      qst.load(q + head, r0, N);
+      dst_.load(dout + head, r0, N);
+      if (t < STG) {
+        const int grow = r0 + t;
+        const size_t gi = (size_t)bh * N + min(grow, N - 1);
+        lse_r = grow < N ? lse[gi] * kLog2e : INFINITY;
+        d_r = grow < N ? dsum[gi] : 0.f;
       }
     }
-    __syncthreads();
+    const uint16_t* Qb = Qs(b);
+    const uint16_t* dOb = dOs(b);
+    const float* lse2s = side + (b * 2 + 0) * STG;
+    const float* dss = side + (b * 2 + 1) * STG;
+    const int r0 = 32 * par;
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int sl = par; sl < SLABS; sl += 2) {
-      const int r0 = 32 * sl;
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int kk = 0; kk < KS; ++kk) {
+      s = mfma32(lds_rowfrag<D>(Qb, r0, kk, lane), kf[kk], s);
+      dp = mfma32(lds_rowfrag<D>(dOb, r0, kk, lane), vf[kk], dp);
+    }
+    // element e: query r0 + acc_row(e, h) of this stage, key = this lane's key
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        s = mfma32(lds_rowfrag<D>(Qs, r0, kk, lane), kf[kk], s);
-        dp = mfma32(lds_rowfrag<D>(dOs, r0, kk, lane), vf[kk], dp);
+    for (int e = 0; e < 16; ++e) {
+      const int qr_ = r0 + acc_row(e, h);
+      const float pe = kvalid ? __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -lse2s[qr_])) : 0.f;
+      s[e] = pe;
+      dp[e] = pe * (dp[e] - dss[qr_]);
+    }
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      bf16x8 ph, pl, dh, dl;
+      split_bf16x8(s, kq, ph, pl);
+      split_bf16x8(dp, kq, dh, dl);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 ob = lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
+        dva[db] = mfma32(ph, ob, dva[db]);
+        dva[db] = mfma32(pl, ob, dva[db]);
+        const bf16x8 qb = lds_colfrag<D>(Qb, r0 + 16 * kq, 32 * db, lane);
+        dka[db] = mfma32(dh, qb, dka[db]);
+        dka[db] = mfma32(dl, qb, dka[db]);
       }
-      // element e: query r0 + acc_row(e, h), key = this lane's key
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qr_ = r0 + acc_row(e, h);
-        const float pe = kvalid ? __builtin_amdgcn_exp2f(s[e] * scale_log2 - lse2s[qr_]) : 0.f;
-        s[e] = pe;
-        dp[e] = pe * (dp[e] - dss[qr_]);
-      }
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq) {
-        bf16x8 ph, pl, dh, dl;
-        split_bf16x8(s, kq, ph, pl);
-        split_bf16x8(dp, kq, dh, dl);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 ob = lds_colfrag<D>(dOs, r0 + 16 * kq, 32 * db, lane);
-          dva[db] = mfma32(ph, ob, dva[db]);
-          dva[db] = mfma32(pl, ob, dva[db]);
-          const bf16x8 qb = lds_colfrag<D>(Qs, r0 + 16 * kq, 32 * db, lane);
-          dka[db] = mfma32(dh, qb, dka[db]);
-          dka[db] = mfma32(dl, qb, dka[db]);
-        }
-      }
+    }
+    qst.store(Qs(b ^ 1));
+    dst_.store(dOs(b ^ 1));
+    if (t < STG) {
+      side[((b ^ 1) * 2 + 0) * STG + t] = lse_r;
+      side[((b ^ 1) * 2 + 1) * STG + t] = d_r;
     }
     __syncthreads();
   }
 
-  // ---- reduce the two query-slab parities and write -----------------------------------
+  // ---- reduce the two slab parities and write ------------------------------------------
   float* red = reinterpret_cast<float*>(smem);  // [kh][K|V][lane][DB*16]
   if (par == 1) {
 #pragma unroll
@@ -255,8 +267,8 @@ __global__ __launch_bounds__(256) void k_dkdv(
         if (krow < N) {
           const size_t off = head + (size_t)krow * D + 32 * db + c;
           if (grad_bf16) {
-            reinterpret_cast<uint16_t*>(dk_out)[off] = (uint16_t)f32_to_bf16_bits(gk);
-            reinterpret_cast<uint16_t*>(dv_out)[off] = (uint16_t)f32_to_bf16_bits(gv);
+            reinterpret_cast<__bf16*>(dk_out)[off] = (__bf16)gk;
+            reinterpret_cast<__bf16*>(dv_out)[off] = (__bf16)gv;
           } else {
             reinterpret_cast<float*>(dk_out)[off] = gk;
             reinterpret_cast<float*>(dv_out)[off] = gv;
@@ -267,22 +279,25 @@ __global__ __launch_bounds__(256) void k_dkdv(
 }
 
 // ------------------------------------------------------------------------------------
-// dQ: one workgroup per query block, one wavefront per 32 query rows.
+// dQ: one workgroup per query block (XCD-contiguous order), one wavefront per 32 rows;
+// K and V tiles staged like the forward pass.
 // ------------------------------------------------------------------------------------
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2) void k_dq(
+__global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int N, int nqb,
-    int nkb, float scale_log2, float scale, void* __restrict__ dq_out, int grad_bf16) {
+    int nkb, int total, float scale_log2, float scale, void* __restrict__ dq_out,
+    int grad_bf16) {
   constexpr int NT = BQ * 2;
-  constexpr int NCH = TileCfg<D>::CHUNKS / NT;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  __shared__ __align__(16) uint16_t smem[2][2][TileCfg<D>::TILE];  // [buf][K|V]
+  __shared__ __align__(16) uint16_t smem[2][2][Tile<D>::ELEMS];  // [buf][K|V]
 
-  const int bh = blockIdx.y, i = blockIdx.x;
+  const int tile_id = xcd_remap(blockIdx.x, total);
+  const int bh = tile_id / nqb;
+  const int i = tile_id - bh * nqb;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c = lane & 31, h = lane >> 5;
   const size_t head = (size_t)bh * N * D;
@@ -293,40 +308,37 @@ __global__ __launch_bounds__(BQ * 2) void k_dq(
 
   const int qrow = i * BQ + 32 * wv + c;
   const bool qvalid = qrow < N;
+  const size_t qoff = head + (size_t)min(qrow, N - 1) * D + 8 * h;
   bf16x8 qf[KS], df[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
-    if (qvalid) {
-      qf[kk] = *reinterpret_cast<const bf16x8*>(q + head + (size_t)qrow * D + 16 * kk + 8 * h);
-      df[kk] = *reinterpret_cast<const bf16x8*>(dout + head + (size_t)qrow * D + 16 * kk + 8 * h);
-    } else {
-      qf[kk] = bf16x8{};
-      df[kk] = bf16x8{};
-    }
+    qf[kk] = *reinterpret_cast<const bf16x8*>(q + qoff + 16 * kk);
+    df[kk] = *reinterpret_cast<const bf16x8*>(dout + qoff + 16 * kk);
   }
-  const float lse2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dq_sum = qvalid ? dsum[(size_t)bh * N + qrow] : 0.f;
+  const size_t ri = (size_t)bh * N + min(qrow, N - 1);
+  const float lse2 = lse[ri] * kLog2e;
+  const float dq_sum = dsum[ri];
 
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  uint4 kr[NCH], vr[NCH];
+  Stager<D, kBlkK, NT> kst, vst;
   if (cnt > 0) {
     const int j0 = list[0];
-    tile_load<D, NT>(kr, kh_, j0 * kBlkK, N);
-    tile_load<D, NT>(vr, vh_, j0 * kBlkK, N);
-    tile_store<D, NT>(kr, smem[0][0]);
-    tile_store<D, NT>(vr, smem[0][1]);
+    kst.load(kh_, j0 * kBlkK, N);
+    vst.load(vh_, j0 * kBlkK, N);
+    kst.store(smem[0][0]);
+    vst.store(smem[0][1]);
   }
   __syncthreads();
   for (int t = 0; t < cnt; ++t) {
     const int buf = t & 1;
     const int j = list[t];
-    if (t + 1 < cnt) {
-      const int jn = list[t + 1];
-      tile_load<D, NT>(kr, kh_, jn * kBlkK, N);
-      tile_load<D, NT>(vr, vh_, jn * kBlkK, N);
+    {  // next tile (the last iteration reloads its own tile; the copy goes unused)
+      const int jn = list[min(t + 1, cnt - 1)];
+      kst.load(kh_, jn * kBlkK, N);
+      vst.load(vh_, jn * kBlkK, N);
     }
     const uint16_t* Ks = smem[buf][0];
     const uint16_t* Vs = smem[buf][1];
@@ -341,15 +353,23 @@ __global__ __launch_bounds__(BQ * 2) void k_dq(
         dp[kb] = mfma32(lds_rowfrag<D>(Vs, 32 * kb, kk, lane), df[kk], dp[kb]);
       }
     }
-    const int key0 = j * kBlkK;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const bool ok = key0 + 32 * kb + acc_row(e, h) < N;
-        const float pe = ok ? __builtin_amdgcn_exp2f(s[kb][e] * scale_log2 - lse2) : 0.f;
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale_log2, -lse2));
         dp[kb][e] = pe * (dp[kb][e] - dq_sum);
       }
+    const int key0 = j * kBlkK;
+    if (key0 + kBlkK > N) {  // keys at or beyond N exist only in the last key block
+      const int lim = N - key0 - 8 * h;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 16 * (e >> 3) + (e & 7);
+        if (r >= lim) dp[0][e] = 0.f;
+        if (r + 32 >= lim) dp[1][e] = 0.f;
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 dh, dl;
@@ -361,10 +381,8 @@ __global__ __launch_bounds__(BQ * 2) void k_dq(
         acc[db] = mfma32(ka, dl, acc[db]);
       }
     }
-    if (t + 1 < cnt) {
-      tile_store<D, NT>(kr, smem[buf ^ 1][0]);
-      tile_store<D, NT>(vr, smem[buf ^ 1][1]);
-    }
+    kst.store(smem[buf ^ 1][0]);
+    vst.store(smem[buf ^ 1][1]);
     __syncthreads();
   }
   if (qvalid) {
@@ -377,10 +395,8 @@ __global__ __launch_bounds__(BQ * 2) void k_dq(
         const float x0 = acc[db][4 * g + 0] * scale, x1 = acc[db][4 * g + 1] * scale;
         const float x2 = acc[db][4 * g + 2] * scale, x3 = acc[db][4 * g + 3] * scale;
         if (grad_bf16) {
-          uint2 pk;
-          pk.x = pack_bf16x2(x0, x1);
-          pk.y = pack_bf16x2(x2, x3);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dq_out) + off) = pk;
+          const bf16x4 pk = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+          *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(dq_out) + off) = pk;
         } else {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(dq_out) + off) =
               make_float4(x0, x1, x2, x3);
@@ -429,14 +445,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
     hipLaunchKernelGGL(k_collists, dim3(nw, (unsigned)g.bh()), dim3(256),
                        g.nqb * sizeof(uint32_t), s, a.bits, g.nqb, g.nkb, nw, a.q_idx, a.q_cnt);
   }
-  if (stages & 2u)
-    hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(g.nkb, (unsigned)g.bh()), dim3(256), 0, s, a.q, a.k,
-                       a.v, a.dout, a.lse, a.dsum, a.q_idx, a.q_cnt, g.N, g.nqb, g.nkb, sl2,
-                       a.scale, a.dk, a.dv, a.grad_bf16);
-  if (stages & 4u)
-    hipLaunchKernelGGL((k_dq<D, BQ>), dim3(g.nqb, (unsigned)g.bh()), dim3(BQ * 2), 0, s, a.q, a.k,
-                       a.v, a.dout, a.lse, a.dsum, a.kv_idx, a.kv_cnt, g.N, g.nqb, g.nkb, sl2,
-                       a.scale, a.dq, a.grad_bf16);
+  if (stages & 2u) {
+    const int total = (int)(g.nkb * g.bh());
+    hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(total), dim3(256), 0, s, a.q, a.k, a.v, a.dout,
+                       a.lse, a.dsum, a.q_idx, a.q_cnt, g.N, g.nqb, g.nkb, total, sl2, a.scale,
+                       a.dk, a.dv, a.grad_bf16);
+  }
+  if (stages & 4u) {
+    const int total = (int)(g.nqb * g.bh());
+    hipLaunchKernelGGL((k_dq<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.dout,
+                       a.lse, a.dsum, a.kv_idx, a.kv_cnt, g.N, g.nqb, g.nkb, total, sl2, a.scale,
+                       a.dq, a.grad_bf16);
+  }
   return hipGetLastError();
 }
 

@@ -3,13 +3,17 @@
 // Kernel-Implementierung und Modellanpassung": dropped tiles cost no matrix product and
 // no softmax).
 //
-// One workgroup per (b, h, query block); one wavefront per 32 query rows.  For each
-// listed key block (64 keys) the K and V tiles are staged row-major in LDS (double
-// buffered, the next tile's global loads in flight during the current tile's math).
+// One workgroup per (b, h, query block), one wavefront per 32 query rows, workgroups
+// ordered so that each XCD works on a contiguous run of query blocks of one head.  For
+// each listed key block (64 keys) the K and V tiles are staged row-major in LDS (double
+// buffered; the next tile's global loads are in flight during the current tile's math).
 // Per wavefront and tile:
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16 (K rows read in perm32 order, Q in
 //                 registers), so every lane holds 32 scores of a single query row;
-//   online softmax in fp32 with exp2 (row max exchanged once with lane l^32);
+//   online softmax in fp32 with exp2; with o_lo requested the running maximum is
+//                 raised only when a tile's maximum exceeds it by more than 8 (log2
+//                 units), so most tiles skip the rescale of O (probabilities stay below
+//                 2^8);
 //   O^T += V^T P^T with V^T read by ds_read_b64_tr_b16; P enters the MFMA as bf16,
 //                 or, when the caller asks for the residual output o_lo, as a bf16
 //                 hi + lo pair so that O is accurate to about 16 bits (the backward
@@ -20,24 +24,25 @@
 
 namespace spa {
 
+
 template <int D, int BQ, bool SPLIT>
-__global__ __launch_bounds__(BQ * 2) void k_fwd(const uint16_t* __restrict__ q,
-                                               const uint16_t* __restrict__ k,
-                                               const uint16_t* __restrict__ v,
-                                               const int32_t* __restrict__ kv_idx,
-                                               const int32_t* __restrict__ kv_cnt, int N,
-                                               int nqb, int nkb, float scale_log2,
-                                               uint16_t* __restrict__ o,
-                                               uint16_t* __restrict__ o_lo,
-                                               float* __restrict__ lse) {
+__global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ q,
+                                                  const uint16_t* __restrict__ k,
+                                                  const uint16_t* __restrict__ v,
+                                                  const int32_t* __restrict__ kv_idx,
+                                                  const int32_t* __restrict__ kv_cnt, int N,
+                                                  int nqb, int nkb, int total, float scale_log2,
+                                                  uint16_t* __restrict__ o,
+                                                  uint16_t* __restrict__ o_lo,
+                                                  float* __restrict__ lse) {
   constexpr int NT = BQ * 2;
-  constexpr int NCH = TileCfg<D>::CHUNKS / NT;
   constexpr int KS = D / 16;  // k-steps over the head dimension
   constexpr int DB = D / 32;  // 32-wide column blocks of O
-  __shared__ __align__(16) uint16_t smem[2][2][TileCfg<D>::TILE];  // [buf][K|V]
+  __shared__ __align__(16) uint16_t smem[2][2][Tile<D>::ELEMS];  // [buf][K|V]
 
-  const int bh = blockIdx.y;
-  const int i = blockIdx.x;
+  const int tile_id = xcd_remap(blockIdx.x, total);
+  const int bh = tile_id / nqb;
+  const int i = tile_id - bh * nqb;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c = lane & 31, h = lane >> 5;
   const size_t head = (size_t)bh * N * D;
@@ -46,91 +51,97 @@ __global__ __launch_bounds__(BQ * 2) void k_fwd(const uint16_t* __restrict__ q,
   const int32_t* list = kv_idx + ((size_t)bh * nqb + i) * nkb;
   const int cnt = kv_cnt[(size_t)bh * nqb + i];
 
-  // this lane's query row and its Q fragments (B operand of S^T = K Q^T)
+  // this lane's query row (B operand of S^T = K Q^T); rows beyond N compute on a copy of
+  // row N-1 and are never written
   const int qrow = i * BQ + 32 * wv + c;
   const bool qvalid = qrow < N;
+  const uint16_t* qsrc = q + head + (size_t)min(qrow, N - 1) * D + 8 * h;
   bf16x8 qf[KS];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    if (qvalid)
-      qf[kk] = *reinterpret_cast<const bf16x8*>(q + head + (size_t)qrow * D + 16 * kk + 8 * h);
-    else
-      qf[kk] = bf16x8{};
-  }
+  for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * kk);
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  uint4 kr[NCH], vr[NCH];
+  Stager<D, kBlkK, NT> kst, vst;
   if (cnt > 0) {
     const int j0 = list[0];
-    tile_load<D, NT>(kr, kh_, j0 * kBlkK, N);
-    tile_load<D, NT>(vr, vh_, j0 * kBlkK, N);
-    tile_store<D, NT>(kr, smem[0][0]);
-    tile_store<D, NT>(vr, smem[0][1]);
+    kst.load(kh_, j0 * kBlkK, N);
+    vst.load(vh_, j0 * kBlkK, N);
+    kst.store(smem[0][0]);
+    vst.store(smem[0][1]);
   }
   __syncthreads();
 
   for (int t = 0; t < cnt; ++t) {
     const int buf = t & 1;
     const int j = list[t];
-    if (t + 1 < cnt) {
-      const int jn = list[t + 1];
-      tile_load<D, NT>(kr, kh_, jn * kBlkK, N);
-      tile_load<D, NT>(vr, vh_, jn * kBlkK, N);
+    {  // next tile (the last iteration reloads its own tile; the copy goes unused)
+      const int jn = list[min(t + 1, cnt - 1)];
+      kst.load(kh_, jn * kBlkK, N);
+      vst.load(vh_, jn * kBlkK, N);
     }
     const uint16_t* Ks = smem[buf][0];
     const uint16_t* Vs = smem[buf][1];
 
     // ---- S^T = K Q^T : two 32-key slabs -------------------------------------------
-    f32x16 s[2];
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) s[kb] = mfma32(lds_rowfrag<D>(Ks, 32 * kb, kk, lane), qf[kk], s[kb]);
+    for (int kk = 0; kk < KS; ++kk) {
+      sc[0] = mfma32(lds_rowfrag<D>(Ks, 0, kk, lane), qf[kk], sc[0]);
+      sc[1] = mfma32(lds_rowfrag<D>(Ks, 32, kk, lane), qf[kk], sc[1]);
     }
-    // ---- online softmax (log2 domain) ---------------------------------------------
+    // keys at or beyond N exist only in the last key block
     const int key0 = j * kBlkK;
-    const bool tail = key0 + kBlkK > N;
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    if (key0 + kBlkK > N) {
+      const int lim = N - key0 - 8 * h;  // element e is valid iff acc_row(e,0) < lim
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float x = s[kb][e] * scale_log2;
-        if (tail && key0 + 32 * kb + acc_row(e, h) >= N) x = -INFINITY;
-        s[kb][e] = x;
-        mloc = fmaxf(mloc, x);
+        const int r = 16 * (e >> 3) + (e & 7);
+        if (r >= lim) sc[0][e] = -INFINITY;
+        if (r + 32 >= lim) sc[1][e] = -INFINITY;
       }
-    mloc = fmaxf(mloc, swap_halves(mloc));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    }
+    // ---- online softmax (log2 domain, scale folded into the exponent) -------------------
+    float mloc = sc[0][0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sc[0][e]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sc[1][e]);
+    mloc = fmaxf(mloc, swap_halves(mloc)) * scale_log2;
+    // With o_lo requested, P's rounding is carried by the lo half and the running maximum
+    // may lag the true one by up to 8 (log2 units).  Without it the maximum is exact, so the
+    // dominant probability of a peaked row is exactly 1 and rounds without error.
+    constexpr float kSlack = SPLIT ? 8.0f : 0.0f;
+    const bool raise = mloc > m_run + kSlack;
+    if (__ballot(raise)) {
+      const float m_new = raise ? mloc : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    }
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(s[kb][e] - m_new);
-        s[kb][e] = pe;
-        psum += pe;
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    for (int e = 0; e < 16; ++e) {
+      sc[0][e] = __builtin_amdgcn_exp2f(fmaf(sc[0][e], scale_log2, -m_run));
+      sc[1][e] = __builtin_amdgcn_exp2f(fmaf(sc[1][e], scale_log2, -m_run));
+      psum += sc[0][e] + sc[1][e];
+    }
+    l_run += psum;
     // ---- O^T += V^T P^T ---------------------------------------------------------------
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 ph, pl;
       if constexpr (SPLIT)
-        split_bf16x8(s[kk >> 1], kk & 1, ph, pl);
+        split_bf16x8(sc[kk >> 1], kk & 1, ph, pl);
       else
-        ph = to_bf16x8(s[kk >> 1], kk & 1);
+        ph = to_bf16x8(sc[kk >> 1], kk & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const bf16x8 va = lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
@@ -138,10 +149,8 @@ __global__ __launch_bounds__(BQ * 2) void k_fwd(const uint16_t* __restrict__ q,
         if constexpr (SPLIT) oacc[db] = mfma32(va, pl, oacc[db]);
       }
     }
-    if (t + 1 < cnt) {
-      tile_store<D, NT>(kr, smem[buf ^ 1][0]);
-      tile_store<D, NT>(vr, smem[buf ^ 1][1]);
-    }
+    kst.store(smem[buf ^ 1][0]);
+    vst.store(smem[buf ^ 1][1]);
     __syncthreads();
   }
 
@@ -155,21 +164,15 @@ __global__ __launch_bounds__(BQ * 2) void k_fwd(const uint16_t* __restrict__ q,
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * db + 8 * g + 4 * h;
-        float x[4];
-        uint32_t hb[4];
+        bf16x4 hv, lv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[e] = oacc[db][4 * g + e] * inv;
-          hb[e] = f32_to_bf16_bits(x[e]);
+          const float x = oacc[db][4 * g + e] * inv;
+          hv[e] = (__bf16)x;
+          lv[e] = (__bf16)(x - (float)hv[e]);
         }
-        *reinterpret_cast<uint2*>(orow + d0) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-        if (SPLIT && o_lo) {
-          uint32_t lb[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) lb[e] = f32_to_bf16_bits(x[e] - bf16_bits_to_f32(hb[e]));
-          *reinterpret_cast<uint2*>(o_lo + head + (size_t)qrow * D + d0) =
-              make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
-        }
+        *reinterpret_cast<bf16x4*>(orow + d0) = hv;
+        if (SPLIT && o_lo) *reinterpret_cast<bf16x4*>(o_lo + head + (size_t)qrow * D + d0) = lv;
       }
     if (h == 0)
       lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
@@ -179,13 +182,14 @@ __global__ __launch_bounds__(BQ * 2) void k_fwd(const uint16_t* __restrict__ q,
 template <int D, int BQ>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const Geometry& g = a.g;
-  dim3 grid(g.nqb, (unsigned)g.bh());
+  const int total = (int)(g.nqb * g.bh());
+  dim3 grid(total);
   if (a.o_lo)
     hipLaunchKernelGGL((k_fwd<D, BQ, true>), grid, dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.kv_idx,
-                       a.kv_cnt, g.N, g.nqb, g.nkb, a.scale * kLog2e, a.o, a.o_lo, a.lse);
+                       a.kv_cnt, g.N, g.nqb, g.nkb, total, a.scale * kLog2e, a.o, a.o_lo, a.lse);
   else
     hipLaunchKernelGGL((k_fwd<D, BQ, false>), grid, dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.kv_idx,
-                       a.kv_cnt, g.N, g.nqb, g.nkb, a.scale * kLog2e, a.o, a.o_lo, a.lse);
+                       a.kv_cnt, g.N, g.nqb, g.nkb, total, a.scale * kLog2e, a.o, a.o_lo, a.lse);
   return hipGetLastError();
 }
 

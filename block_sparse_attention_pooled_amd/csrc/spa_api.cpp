@@ -4,7 +4,7 @@
 #include <cmath>
 #include <climits>
 
-#include "../../include/spa.h"
+#include "spa.h"
 #include "spa_internal.h"
 
 namespace {

@@ -100,7 +100,8 @@ def full_check(torch, w, k_frac, p, tag):
     check_close("O", res["o"], o)
     check_close("O without residual", res["o_plain"], o)
     check_close("LSE", res["lse"], lse)
-    assert np.array_equal(res["lse"], res["lse_plain"])
+    # the two forward modes round the running maximum differently; LSE agrees to fp32 ulps
+    np.testing.assert_allclose(res["lse"], res["lse_plain"], rtol=4e-7, atol=4e-7)
     # o + o_lo carries O to ~16 bits
     ok_full, mx_full, _, _ = parity.close(res["o_full"], o, atol=2e-4, rtol_l2=1e-4)
     log(f"  O + o_lo: max_abs={mx_full:.3e}")
