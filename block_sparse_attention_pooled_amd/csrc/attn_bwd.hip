@@ -110,14 +110,16 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
 }
 
 // ------------------------------------------------------------------------------------
-// dK, dV: one workgroup per key block (workgroups in XCD-contiguous order), 4 wavefronts.
-// The key block's query-block list is walked in 64-row stages (a 128-row query block is
-// two stages); Q and dO of the next stage are loaded while the current one is used.
-// Wavefront w owns keys 32*(w&1) .. +32 of the block and the 32-row slab w>>1 of each
-// stage; the two slab parities are summed at the end in a fixed order.
+// dK, dV: one workgroup per key block (workgroups in XCD-contiguous order), 4 wavefronts,
+// one workgroup per CU.  The key block's query-block list is walked one query block per
+// stage; Q and dO of the next query block stream into the other LDS buffer with direct
+// global->LDS loads while the current one is used.  Wavefront w owns keys
+// 32*(w&1) .. +32 of the block and the 32-row slabs of parity w>>1 (two independent
+// slabs per stage when the block has 128 rows); the two parities are summed at the end
+// in a fixed order.
 // ------------------------------------------------------------------------------------
 template <int D, int BQ>
-__global__ __launch_bounds__(256) void k_dkdv(
+__global__ __launch_bounds__(256, 1) void k_dkdv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum,
@@ -126,16 +128,14 @@ __global__ __launch_bounds__(256) void k_dkdv(
     void* __restrict__ dv_out, int grad_bf16) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int STG = 64;                 // query rows per stage
-  constexpr int SPB = BQ / STG;           // stages per query block
-  constexpr int TILE = STG * D;           // elements of one staged Q or dO tile
-  constexpr int STAGE_BYTES = 2 * (2 * TILE * 2 + 2 * STG * 4);  // 2 buffers: Q, dO, lse2, D
-  constexpr int RED_BYTES = 2 * 2 * 64 * DB * 16 * 4;            // dK, dV partials
+  constexpr int SLABS = BQ / 32;          // 32-row slabs per query block
+  constexpr int TILE = BQ * D;            // elements of one staged Q or dO tile
+  constexpr int STAGE_BYTES = 2 * (2 * TILE * 2 + 2 * BQ * 4);  // 2 buffers: Q, dO, lse2, D
+  constexpr int RED_BYTES = 2 * 2 * 64 * DB * 16 * 4;           // dK, dV partials
   constexpr int SMEM = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
   __shared__ __align__(16) unsigned char smem[SMEM];
-  auto Qs = [&](int b) { return reinterpret_cast<uint16_t*>(smem) + b * 2 * TILE; };
-  auto dOs = [&](int b) { return reinterpret_cast<uint16_t*>(smem) + b * 2 * TILE + TILE; };
-  float* side = reinterpret_cast<float*>(smem + 2 * 2 * TILE * 2);  // [buf][lse2 | D][STG]
+  uint16_t* tiles = reinterpret_cast<uint16_t*>(smem);           // [buf][Q | dO][TILE]
+  float* side = reinterpret_cast<float*>(smem + 2 * 2 * TILE * 2);  // [buf][lse2 | D][BQ], 16-byte aligned
 
   const int tile_id = xcd_remap(blockIdx.x, total);
   const int bh = tile_id / nkb;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void k_dkdv(
   const int kh = wv & 1, par = wv >> 1;
   const size_t head = (size_t)bh * N * D;
   const int key = j * kBlkK + 32 * kh + c;  // this lane's key (B operand column)
-  const bool kvalid = key < N;
+  const float kmask = key < N ? 1.f : 0.f;  // keys beyond N compute on a copy and get P = 0
 
   bf16x8 kf[KS], vf[KS];
   {
@@ -164,82 +164,88 @@ __global__ __launch_bounds__(256) void k_dkdv(
   }
 
   const int32_t* list = q_idx + ((size_t)bh * nkb + j) * nqb;
-  const int nstage = q_cnt[(size_t)bh * nkb + j] * SPB;
-  // staging of stage st: Q and dO rows [r0, r0 + 64) plus their lse2 and D values
-  Stager<D, STG, 256> qst, dst_;
-  float lse_r = 0.f, d_r = 0.f;
-  if (nstage > 0) {
+  const int cnt = q_cnt[(size_t)bh * nkb + j];
+  float lse_r = 0.f, d_r = 0.f;  // side values of row t (t < BQ) of the staged block
+  if (cnt > 0) {
     const int r0 = list[0] * BQ;
-    qst.load(q + head, r0, N);
-    dst_.load(dout + head, r0, N);
-    if (t < STG) {
+    tile_load_lds<D, BQ, 4>(q + head, r0, N, tiles);
+    tile_load_lds<D, BQ, 4>(dout + head, r0, N, tiles + TILE);
+    if (t < BQ) {
       const int grow = r0 + t;
       const size_t gi = (size_t)bh * N + min(grow, N - 1);
-      lse_r = grow < N ? lse[gi] * kLog2e : INFINITY;  // rows beyond N get P = 0
-      d_r = grow < N ? dsum[gi] : 0.f;
+      side[t] = grow < N ? lse[gi] * kLog2e : INFINITY;  // rows beyond N get P = 0
+      side[BQ + t] = grow < N ? dsum[gi] : 0.f;
     }
-    qst.store(Qs(0));
-    dst_.store(dOs(0));
-    if (t < STG) {
-      side[0 * STG + t] = lse_r;
-      side[1 * STG + t] = d_r;
-    }
+    wait_vmem();
   }
   __syncthreads();
-  for (int st = 0; st < nstage; ++st) {
-    const int b = st & 1;
-    {  // next stage (the last stage reloads itself; the copy goes unused)
-      const int sn = min(st + 1, nstage - 1);
-      const int r0 = list[sn / SPB] * BQ + (sn % SPB) * STG;
-      qst.load(q + head, r0, N);
-      dst_.load(dout + head, r0, N);
-      if (t < STG) {
+  for (int it = 0; it < cnt; ++it) {
+    const int b = it & 1;
+    {  // next query block (the last iteration reloads its own block; the copy goes unused)
+      const int r0 = list[min(it + 1, cnt - 1)] * BQ;
+      uint16_t* nb = tiles + (b ^ 1) * 2 * TILE;
+      tile_load_lds<D, BQ, 4>(q + head, r0, N, nb);
+      tile_load_lds<D, BQ, 4>(dout + head, r0, N, nb + TILE);
+      if (t < BQ) {
         const int grow = r0 + t;
         const size_t gi = (size_t)bh * N + min(grow, N - 1);
         lse_r = grow < N ? lse[gi] * kLog2e : INFINITY;
         d_r = grow < N ? dsum[gi] : 0.f;
       }
     }
-    const uint16_t* Qb = Qs(b);
-    const uint16_t* dOb = dOs(b);
-    const float* lse2s = side + (b * 2 + 0) * STG;
-    const float* dss = side + (b * 2 + 1) * STG;
-    const int r0 = 32 * par;
-    f32x16 s = f32x16{}, dp = f32x16{};
+    const uint16_t* Qb = tiles + b * 2 * TILE;
+    const uint16_t* dOb = Qb + TILE;
+    const float* lse2s = side + b * 2 * BQ;
+    const float* dss = lse2s + BQ;
+#pragma unroll 1
+    for (int sl = par; sl < SLABS; sl += 2) {
+      const int r0 = 32 * sl;
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      s = mfma32(lds_rowfrag<D>(Qb, r0, kk, lane), kf[kk], s);
-      dp = mfma32(lds_rowfrag<D>(dOb, r0, kk, lane), vf[kk], dp);
-    }
-    // element e: query r0 + acc_row(e, h) of this stage, key = this lane's key
+      for (int kk = 0; kk < KS; ++kk) {
+        s = mfma32(lds_rowfrag<D>(Qb, r0, kk, lane), kf[kk], s);
+        dp = mfma32(lds_rowfrag<D>(dOb, r0, kk, lane), vf[kk], dp);
+      }
+      // element e: query r0 + acc_row(e, h) of this block (two runs of 8 rows),
+      // key = this lane's key
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int qr_ = r0 + acc_row(e, h);
-      const float pe = kvalid ? __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -lse2s[qr_])) : 0.f;
-      s[e] = pe;
-      dp[e] = pe * (dp[e] - dss[qr_]);
-    }
+      for (int run = 0; run < 2; ++run) {
+        const int q0 = r0 + 16 * run + 8 * h;
+        const float4 l0 = *reinterpret_cast<const float4*>(lse2s + q0);
+        const float4 l1 = *reinterpret_cast<const float4*>(lse2s + q0 + 4);
+        const float4 d0 = *reinterpret_cast<const float4*>(dss + q0);
+        const float4 d1 = *reinterpret_cast<const float4*>(dss + q0 + 4);
+        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const float dv_[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
-    for (int kq = 0; kq < 2; ++kq) {
-      bf16x8 ph, pl, dh, dl;
-      split_bf16x8(s, kq, ph, pl);
-      split_bf16x8(dp, kq, dh, dl);
+        for (int u = 0; u < 8; ++u) {
+          const int e = 8 * run + u;
+          const float pe = kmask * __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -lv[u]));
+          s[e] = pe;
+          dp[e] = pe * (dp[e] - dv_[u]);
+        }
+      }
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 ob = lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
-        dva[db] = mfma32(ph, ob, dva[db]);
-        dva[db] = mfma32(pl, ob, dva[db]);
-        const bf16x8 qb = lds_colfrag<D>(Qb, r0 + 16 * kq, 32 * db, lane);
-        dka[db] = mfma32(dh, qb, dka[db]);
-        dka[db] = mfma32(dl, qb, dka[db]);
+      for (int kq = 0; kq < 2; ++kq) {
+        bf16x8 ph, pl, dh, dl;
+        split_bf16x8(s, kq, ph, pl);
+        split_bf16x8(dp, kq, dh, dl);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 ob = lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
+          dva[db] = mfma32(ph, ob, dva[db]);
+          dva[db] = mfma32(pl, ob, dva[db]);
+          const bf16x8 qb = lds_colfrag<D>(Qb, r0 + 16 * kq, 32 * db, lane);
+          dka[db] = mfma32(dh, qb, dka[db]);
+          dka[db] = mfma32(dl, qb, dka[db]);
+        }
       }
     }
-    qst.store(Qs(b ^ 1));
-    dst_.store(dOs(b ^ 1));
-    if (t < STG) {
-      side[((b ^ 1) * 2 + 0) * STG + t] = lse_r;
-      side[((b ^ 1) * 2 + 1) * STG + t] = d_r;
+    if (t < BQ) {
+      side[(b ^ 1) * 2 * BQ + t] = lse_r;
+      side[(b ^ 1) * 2 * BQ + BQ + t] = d_r;
     }
+    wait_vmem();
     __syncthreads();
   }
 
@@ -323,66 +329,58 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  Stager<D, kBlkK, NT> kst, vst;
   if (cnt > 0) {
     const int j0 = list[0];
-    kst.load(kh_, j0 * kBlkK, N);
-    vst.load(vh_, j0 * kBlkK, N);
-    kst.store(smem[0][0]);
-    vst.store(smem[0][1]);
+    tile_load_lds<D, kBlkK, NT / 64>(kh_, j0 * kBlkK, N, smem[0][0]);
+    tile_load_lds<D, kBlkK, NT / 64>(vh_, j0 * kBlkK, N, smem[0][1]);
+    wait_vmem();
   }
   __syncthreads();
   for (int t = 0; t < cnt; ++t) {
     const int buf = t & 1;
     const int j = list[t];
-    {  // next tile (the last iteration reloads its own tile; the copy goes unused)
+    {  // next tile streams into the other buffer (the last iteration reloads its own
+       // tile; the copy goes unused)
       const int jn = list[min(t + 1, cnt - 1)];
-      kst.load(kh_, jn * kBlkK, N);
-      vst.load(vh_, jn * kBlkK, N);
+      tile_load_lds<D, kBlkK, NT / 64>(kh_, jn * kBlkK, N, smem[buf ^ 1][0]);
+      tile_load_lds<D, kBlkK, NT / 64>(vh_, jn * kBlkK, N, smem[buf ^ 1][1]);
     }
     const uint16_t* Ks = smem[buf][0];
     const uint16_t* Vs = smem[buf][1];
-    f32x16 s[2], dp[2];
+    const int key0 = j * kBlkK;
+    // one 32-key slab at a time: scores, dP, dS, then its two 16-key steps of dQ
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        s[kb] = mfma32(lds_rowfrag<D>(Ks, 32 * kb, kk, lane), qf[kk], s[kb]);
-        dp[kb] = mfma32(lds_rowfrag<D>(Vs, 32 * kb, kk, lane), df[kk], dp[kb]);
+        s = mfma32(lds_rowfrag<D>(Ks, 32 * kb, kk, lane), qf[kk], s);
+        dp = mfma32(lds_rowfrag<D>(Vs, 32 * kb, kk, lane), df[kk], dp);
       }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][e], scale_log2, -lse2));
-        dp[kb][e] = pe * (dp[kb][e] - dq_sum);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -lse2));
+        dp[e] = pe * (dp[e] - dq_sum);
       }
-    const int key0 = j * kBlkK;
-    if (key0 + kBlkK > N) {  // keys at or beyond N exist only in the last key block
-      const int lim = N - key0 - 8 * h;
+      if (key0 + kBlkK > N) {  // keys at or beyond N exist only in the last key block
+        const int lim = N - key0 - 32 * kb - 8 * h;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = 16 * (e >> 3) + (e & 7);
-        if (r >= lim) dp[0][e] = 0.f;
-        if (r + 32 >= lim) dp[1][e] = 0.f;
+        for (int e = 0; e < 16; ++e)
+          if (16 * (e >> 3) + (e & 7) >= lim) dp[e] = 0.f;
       }
-    }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 dh, dl;
-      split_bf16x8(dp[kk >> 1], kk & 1, dh, dl);
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 dh, dl;
+        split_bf16x8(dp, half, dh, dl);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 ka = lds_colfrag<D>(Ks, 16 * kk, 32 * db, lane);
-        acc[db] = mfma32(ka, dh, acc[db]);
-        acc[db] = mfma32(ka, dl, acc[db]);
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 ka = lds_colfrag<D>(Ks, 32 * kb + 16 * half, 32 * db, lane);
+          acc[db] = mfma32(ka, dh, acc[db]);
+          acc[db] = mfma32(ka, dl, acc[db]);
+        }
       }
     }
-    kst.store(smem[buf ^ 1][0]);
-    vst.store(smem[buf ^ 1][1]);
+    wait_vmem();
     __syncthreads();
   }
   if (qvalid) {

@@ -5,8 +5,9 @@
 //
 // One workgroup per (b, h, query block), one wavefront per 32 query rows, workgroups
 // ordered so that each XCD works on a contiguous run of query blocks of one head.  For
-// each listed key block (64 keys) the K and V tiles are staged row-major in LDS (double
-// buffered; the next tile's global loads are in flight during the current tile's math).
+// each listed key block (64 keys) the K and V tiles stream row-major into LDS with
+// direct global->LDS loads, double buffered: the next tile is in flight while the
+// current one is used.
 // Per wavefront and tile:
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16 (K rows read in perm32 order, Q in
 //                 registers), so every lane holds 32 scores of a single query row;
@@ -65,23 +66,22 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  Stager<D, kBlkK, NT> kst, vst;
   if (cnt > 0) {
     const int j0 = list[0];
-    kst.load(kh_, j0 * kBlkK, N);
-    vst.load(vh_, j0 * kBlkK, N);
-    kst.store(smem[0][0]);
-    vst.store(smem[0][1]);
+    tile_load_lds<D, kBlkK, NT / 64>(kh_, j0 * kBlkK, N, smem[0][0]);
+    tile_load_lds<D, kBlkK, NT / 64>(vh_, j0 * kBlkK, N, smem[0][1]);
+    wait_vmem();
   }
   __syncthreads();
 
   for (int t = 0; t < cnt; ++t) {
     const int buf = t & 1;
     const int j = list[t];
-    {  // next tile (the last iteration reloads its own tile; the copy goes unused)
+    {  // next tile streams into the other buffer (the last iteration reloads its own
+       // tile; the copy goes unused)
       const int jn = list[min(t + 1, cnt - 1)];
-      kst.load(kh_, jn * kBlkK, N);
-      vst.load(vh_, jn * kBlkK, N);
+      tile_load_lds<D, kBlkK, NT / 64>(kh_, jn * kBlkK, N, smem[buf ^ 1][0]);
+      tile_load_lds<D, kBlkK, NT / 64>(vh_, jn * kBlkK, N, smem[buf ^ 1][1]);
     }
     const uint16_t* Ks = smem[buf][0];
     const uint16_t* Vs = smem[buf][1];
@@ -149,8 +149,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
         if constexpr (SPLIT) oacc[db] = mfma32(va, pl, oacc[db]);
       }
     }
-    kst.store(smem[buf ^ 1][0]);
-    vst.store(smem[buf ^ 1][1]);
+    wait_vmem();
     __syncthreads();
   }
 

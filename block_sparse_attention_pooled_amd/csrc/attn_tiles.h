@@ -56,6 +56,33 @@ struct Stager {
   }
 };
 
+// Direct global -> LDS staging (global_load_lds_dwordx4): each wave instruction writes
+// 64 lanes x 16 bytes to one contiguous 1 KB LDS segment (lane l at byte 16*l), so the
+// swizzle is applied on the global side: lane l of segment s fetches the chunk that
+// belongs at LDS chunk 64*s + l.  Rows at or beyond N are fetched from row N-1.
+// The caller waits (vmcnt) and synchronises before reading the tile.
+template <int D, int NROWS, int NWAVES>
+__device__ __forceinline__ void tile_load_lds(const uint16_t* __restrict__ base, int row0, int N,
+                                              uint16_t* lds) {
+  constexpr int SEGS = NROWS * D * 2 / 1024;   // 1 KB segments per tile
+  constexpr int PER = SEGS / NWAVES;
+  constexpr int RPS = 1024 / (D * 2);          // rows per segment
+  static_assert(SEGS % NWAVES == 0, "segments must divide among the waves");
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int seg = wv * PER + u;
+    const int row = seg * RPS + lane / Tile<D>::CPR;
+    const int pc = lane % Tile<D>::CPR;
+    const int cc = pc ^ Tile<D>::swz(row);
+    const int grow = min(row0 + row, N - 1);
+    __builtin_amdgcn_global_load_lds(base + (size_t)grow * D + cc * 8,
+                                     (SPA_LDS void*)(lds + seg * 512), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // A (or B) operand holding X[r0 + perm32(c)][16*kk + 8*h .. +7] for lane c + 32*h.
 template <int D>
 __device__ __forceinline__ bf16x8 lds_rowfrag(const uint16_t* lds, int r0, int kk, int lane) {
@@ -75,24 +102,36 @@ __device__ __forceinline__ bf16x8 lds_colfrag(const uint16_t* lds, int r0, int c
   return join_bf16x8(lo, hi);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// round-to-nearest-even of a float pair into one packed register (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& x, int half) {
-  bf16x8 r;
+  uint32_t w[4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) r[t] = (__bf16)x[8 * half + t];
-  return r;
+  for (int t = 0; t < 4; ++t) w[t] = pk_bf16(x[8 * half + 2 * t], x[8 * half + 2 * t + 1]);
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 // Elements 8*half .. 8*half+7 of x as a bf16 pair hi + lo with hi = RNE(x) and
 // lo = RNE(x - hi): the pair carries about 16 significant bits, so an MFMA fed with
 // both halves loses almost nothing to the bf16 operand format.
 __device__ __forceinline__ void split_bf16x8(const f32x16& x, int half, bf16x8& hi, bf16x8& lo) {
+  uint32_t wh[4], wl[4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const float v = x[8 * half + t];
-    const __bf16 hv = (__bf16)v;
-    hi[t] = hv;
-    lo[t] = (__bf16)(v - (float)hv);
+  for (int t = 0; t < 4; ++t) {
+    const float a = x[8 * half + 2 * t], b = x[8 * half + 2 * t + 1];
+    const uint32_t p = pk_bf16(a, b);
+    wh[t] = p;
+    wl[t] = pk_bf16(a - __uint_as_float(p << 16), b - __uint_as_float(p & 0xFFFF0000u));
   }
+  hi = __builtin_bit_cast(bf16x8, wh);
+  lo = __builtin_bit_cast(bf16x8, wl);
 }
 
 // Workgroup order: the hardware deals consecutive workgroup ids round-robin to the 8
