@@ -118,6 +118,69 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
 // slabs per stage when the block has 128 rows); the two parities are summed at the end
 // in a fixed order.
 // ------------------------------------------------------------------------------------
+// One 32-row query slab of a staged block against this wave's 32 keys.
+// S = Q K^T and dP = dO V^T with lanes owning keys (K, V fragments in registers).
+template <int D>
+__device__ __forceinline__ void slab_scores(const uint16_t* Qb, const uint16_t* dOb, int r0,
+                                            const bf16x8 (&kf)[D / 16],
+                                            const bf16x8 (&vf)[D / 16], int lane, f32x16& s,
+                                            f32x16& dp) {
+  s = f32x16{};
+  dp = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    s = mfma32(lds_rowfrag<D>(Qb, r0, kk, lane), kf[kk], s);
+    dp = mfma32(lds_rowfrag<D>(dOb, r0, kk, lane), vf[kk], dp);
+  }
+}
+
+// P = exp2(S*scale*log2e - lse2) and dS = P (dP - D), in place; element e belongs to
+// query row r0 + acc_row(e, h) (two runs of 8 consecutive rows).
+__device__ __forceinline__ void slab_probs(const float* lse2s, const float* dss, int r0, int h,
+                                           float kmask, float scale_log2, f32x16& s,
+                                           f32x16& dp) {
+#pragma unroll
+  for (int run = 0; run < 2; ++run) {
+    const int q0 = r0 + 16 * run + 8 * h;
+    const float4 l0 = *reinterpret_cast<const float4*>(lse2s + q0);
+    const float4 l1 = *reinterpret_cast<const float4*>(lse2s + q0 + 4);
+    const float4 d0 = *reinterpret_cast<const float4*>(dss + q0);
+    const float4 d1 = *reinterpret_cast<const float4*>(dss + q0 + 4);
+    const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+    const float dv_[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = 8 * run + u;
+      const float pe = kmask * __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -lv[u]));
+      s[e] = pe;
+      dp[e] = pe * (dp[e] - dv_[u]);
+    }
+  }
+}
+
+// dV += P^T dO and dK += dS^T Q for the slab (P, dS as bf16 hi + lo pairs; dO^T, Q^T
+// gathered with transpose reads).
+template <int D>
+__device__ __forceinline__ void slab_grads(const uint16_t* Qb, const uint16_t* dOb, int r0,
+                                           int lane, const f32x16& p, const f32x16& ds,
+                                           f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq) {
+    bf16x8 ph, pl, dh, dl;
+    split_bf16x8(p, kq, ph, pl);
+    split_bf16x8(ds, kq, dh, dl);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const bf16x8 ob = lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
+      dva[db] = mfma32(ph, ob, dva[db]);
+      dva[db] = mfma32(pl, ob, dva[db]);
+      const bf16x8 qb = lds_colfrag<D>(Qb, r0 + 16 * kq, 32 * db, lane);
+      dka[db] = mfma32(dh, qb, dka[db]);
+      dka[db] = mfma32(dl, qb, dka[db]);
+    }
+  }
+}
+
 template <int D, int BQ>
 __global__ __launch_bounds__(256, 1) void k_dkdv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -197,49 +260,23 @@ __global__ __launch_bounds__(256, 1) void k_dkdv(
     const uint16_t* dOb = Qb + TILE;
     const float* lse2s = side + b * 2 * BQ;
     const float* dss = lse2s + BQ;
-#pragma unroll 1
-    for (int sl = par; sl < SLABS; sl += 2) {
-      const int r0 = 32 * sl;
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        s = mfma32(lds_rowfrag<D>(Qb, r0, kk, lane), kf[kk], s);
-        dp = mfma32(lds_rowfrag<D>(dOb, r0, kk, lane), vf[kk], dp);
-      }
-      // element e: query r0 + acc_row(e, h) of this block (two runs of 8 rows),
-      // key = this lane's key
-#pragma unroll
-      for (int run = 0; run < 2; ++run) {
-        const int q0 = r0 + 16 * run + 8 * h;
-        const float4 l0 = *reinterpret_cast<const float4*>(lse2s + q0);
-        const float4 l1 = *reinterpret_cast<const float4*>(lse2s + q0 + 4);
-        const float4 d0 = *reinterpret_cast<const float4*>(dss + q0);
-        const float4 d1 = *reinterpret_cast<const float4*>(dss + q0 + 4);
-        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const float dv_[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = 8 * run + u;
-          const float pe = kmask * __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -lv[u]));
-          s[e] = pe;
-          dp[e] = pe * (dp[e] - dv_[u]);
-        }
-      }
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq) {
-        bf16x8 ph, pl, dh, dl;
-        split_bf16x8(s, kq, ph, pl);
-        split_bf16x8(dp, kq, dh, dl);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 ob = lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
-          dva[db] = mfma32(ph, ob, dva[db]);
-          dva[db] = mfma32(pl, ob, dva[db]);
-          const bf16x8 qb = lds_colfrag<D>(Qb, r0 + 16 * kq, 32 * db, lane);
-          dka[db] = mfma32(dh, qb, dka[db]);
-          dka[db] = mfma32(dl, qb, dka[db]);
-        }
-      }
+    if constexpr (SLABS == 4) {
+      // two independent slabs per wave, software-pipelined: the MFMAs of one slab are
+      // issued next to the VALU work of the other
+      const int ra = 32 * par, rb = 32 * (par + 2);
+      f32x16 sa, dpa, sb, dpb;
+      slab_scores<D>(Qb, dOb, ra, kf, vf, lane, sa, dpa);
+      slab_scores<D>(Qb, dOb, rb, kf, vf, lane, sb, dpb);
+      slab_probs(lse2s, dss, ra, h, kmask, scale_log2, sa, dpa);
+      slab_grads<D>(Qb, dOb, ra, lane, sa, dpa, dka, dva);
+      slab_probs(lse2s, dss, rb, h, kmask, scale_log2, sb, dpb);
+      slab_grads<D>(Qb, dOb, rb, lane, sb, dpb, dka, dva);
+    } else {
+      const int ra = 32 * par;
+      f32x16 sa, dpa;
+      slab_scores<D>(Qb, dOb, ra, kf, vf, lane, sa, dpa);
+      slab_probs(lse2s, dss, ra, h, kmask, scale_log2, sa, dpa);
+      slab_grads<D>(Qb, dOb, ra, lane, sa, dpa, dka, dva);
     }
     if (t < BQ) {
       side[(b ^ 1) * 2 * BQ + t] = lse_r;
@@ -250,14 +287,15 @@ __global__ __launch_bounds__(256, 1) void k_dkdv(
   }
 
   // ---- reduce the two slab parities and write ------------------------------------------
-  float* red = reinterpret_cast<float*>(smem);  // [kh][K|V][lane][DB*16]
+  float* red = reinterpret_cast<float*>(smem);  // [kh][K|V][DB*16][lane]: lane-contiguous
+  auto slot = [&](int which, int idx) { return ((kh * 2 + which) * (DB * 16) + idx) * 64 + lane; };
   if (par == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        red[((kh * 2 + 0) * 64 + lane) * (DB * 16) + db * 16 + e] = dka[db][e];
-        red[((kh * 2 + 1) * 64 + lane) * (DB * 16) + db * 16 + e] = dva[db][e];
+        red[slot(0, db * 16 + e)] = dka[db][e];
+        red[slot(1, db * 16 + e)] = dva[db][e];
       }
   }
   __syncthreads();
@@ -266,8 +304,8 @@ __global__ __launch_bounds__(256, 1) void k_dkdv(
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float gk = (dka[db][e] + red[((kh * 2 + 0) * 64 + lane) * (DB * 16) + db * 16 + e]) * scale;
-        const float gv = dva[db][e] + red[((kh * 2 + 1) * 64 + lane) * (DB * 16) + db * 16 + e];
+        const float gk = (dka[db][e] + red[slot(0, db * 16 + e)]) * scale;
+        const float gv = dva[db][e] + red[slot(1, db * 16 + e)];
         // accumulator element e: key row 8*(e/4) + 4*h + e%4 of this wave's 32 keys, column c
         const int krow = j * kBlkK + 32 * kh + 8 * (e >> 2) + 4 * h + (e & 3);
         if (krow < N) {

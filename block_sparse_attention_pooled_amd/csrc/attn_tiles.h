@@ -6,13 +6,12 @@
 namespace spa {
 
 // LDS layout of a row-major [rows, D] bf16 tile: rows are unpadded and the 16-byte chunks
-// of row r are XOR-permuted by swz(r).  With this permutation
+// of row r are XOR-permuted by swz(r), a rotation of the row's low four bits.  With it
 //   - the 16 rows read by 16 consecutive lanes of a perm32-ordered A operand
-//     (ds_read_b128) fall on 16 distinct 16-byte bank groups, and every 8 consecutive
-//     lanes on 8 distinct ones;
-//   - the 4 rows x 32 bytes read by a 16-lane group of ds_read_b64_tr_b16 fall on
-//     8 distinct 16-byte bank groups;
-// so neither access pattern has bank conflicts (for D = 128).
+//     (ds_read_b128) fall on 16 distinct 16-byte chunks of a 256-byte bank window;
+//   - the 4 rows x 64 bytes read by 32 consecutive lanes of ds_read_b64_tr_b16 fall on
+//     16 distinct chunks;
+// and the LDS bank-conflict counter reads zero for all three attention kernels (D = 128).
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
@@ -20,7 +19,7 @@ struct Tile {
   static constexpr int ELEMS = ROWS * D;
   __device__ __forceinline__ static int swz(int r) {
     if constexpr (D == 128)
-      return ((r & 3) << 1) | ((r >> 3) & 1) | ((r & 4) << 1);
+      return ((r & 3) << 2) | ((r >> 2) & 3);
     else
       return ((r & 3) << 1) | ((r >> 3) & 1);
   }
