@@ -24,19 +24,27 @@
 namespace spa {
 
 // ------------------------------------------------------------------------------------
-// D = rowsum(dO * O)
+// Per-row side values, padded to whole query blocks: D = rowsum(dO * O) and
+// lse2 = lse * log2(e).  Rows at or beyond N (padding) get D = 0 and lse2 = +inf, so that
+// their probabilities evaluate to exactly 0 wherever a staged tile holds such a row.
 // ------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_dsum(const uint16_t* __restrict__ o,
                                               const uint16_t* __restrict__ o_lo,
-                                              const uint16_t* __restrict__ dout, long long rows,
-                                              float* __restrict__ dsum) {
+                                              const uint16_t* __restrict__ dout,
+                                              const float* __restrict__ lse, int N, int npad,
+                                              long long rows, float* __restrict__ dsum,
+                                              float* __restrict__ lse2) {
   constexpr int CPR = D / 8;         // lanes per row
   constexpr int RPB = 256 / CPR;     // rows per block
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / CPR;
+  const long long prow = (long long)blockIdx.x * RPB + threadIdx.x / CPR;  // padded index
   const int cc = threadIdx.x % CPR;
+  const long long bh = prow / npad;
+  const int r = (int)(prow - bh * npad);
+  const bool real = prow < rows && r < N;
+  const long long row = bh * N + r;  // unpadded index, valid when real
   float acc = 0.f;
-  if (row < rows) {
+  if (real) {
     const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + cc * 8);
     const uint4 b = *reinterpret_cast<const uint4*>(dout + row * D + cc * 8);
     const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
@@ -58,7 +66,10 @@ __global__ __launch_bounds__(256) void k_dsum(const uint16_t* __restrict__ o,
   }
 #pragma unroll
   for (int off = CPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && cc == 0) dsum[row] = acc;
+  if (prow < rows && cc == 0) {
+    dsum[prow] = acc;
+    lse2[prow] = real ? lse[row] * kLog2e : INFINITY;
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -110,213 +121,285 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
 }
 
 // ------------------------------------------------------------------------------------
-// dK, dV: one workgroup per key block (workgroups in XCD-contiguous order), 4 wavefronts,
-// one workgroup per CU.  The key block's query-block list is walked one query block per
-// stage; Q and dO of the next query block stream into the other LDS buffer with direct
-// global->LDS loads while the current one is used.  Wavefront w owns keys
-// 32*(w&1) .. +32 of the block and the 32-row slabs of parity w>>1 (two independent
-// slabs per stage when the block has 128 rows); the two parities are summed at the end
-// in a fixed order.
+// dK, dV: one workgroup per key block (workgroups in XCD-contiguous order), 8 wavefronts,
+// one workgroup per CU.  The key block's query-block list is walked in stages of 64 query
+// rows; Q and dO of each stage stream into a ring of three LDS slots with direct
+// global->LDS loads, two stages ahead of their last use.
+//
+// The 64 keys x 64 rows of a stage split into four units (32 keys x 32 rows).  Each
+// unit has two wavefronts with different jobs, placed so that they share a SIMD:
+//   producer (waves 0-3):  S = Q K^T (K fragments in registers), P = exp2(S c - lse2),
+//                          P to LDS (fp32), dV += P^T dO with P as a bf16 hi + lo pair;
+//   consumer (waves 4-7):  one stage behind, dP = dO V^T (V fragments in registers),
+//                          P from LDS, dS = P (dP - D), dK += dS^T Q with dS as a bf16
+//                          hi + lo pair.
+// The two jobs of a SIMD interleave freely (one wavefront's exp and conversions run
+// while the other's MFMAs execute).  Each wavefront's partial sums cover its 32-row
+// slab of every stage; the two slabs are added at the end in a fixed order.
 // ------------------------------------------------------------------------------------
-// One 32-row query slab of a staged block against this wave's 32 keys.
-// S = Q K^T and dP = dO V^T with lanes owning keys (K, V fragments in registers).
-template <int D>
-__device__ __forceinline__ void slab_scores(const uint16_t* Qb, const uint16_t* dOb, int r0,
-                                            const bf16x8 (&kf)[D / 16],
-                                            const bf16x8 (&vf)[D / 16], int lane, f32x16& s,
-                                            f32x16& dp) {
-  s = f32x16{};
-  dp = f32x16{};
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    s = mfma32(lds_rowfrag<D>(Qb, r0, kk, lane), kf[kk], s);
-    dp = mfma32(lds_rowfrag<D>(dOb, r0, kk, lane), vf[kk], dp);
-  }
+// Loads of stage st (64 query rows of query block qb) into one ring slot: the Q and dO
+// tiles and the lse2 / D rows (one 4-byte direct load per lane).  Q and dO rows at or
+// beyond N read as zeros; their lse2 of +inf makes their P exactly 0.
+struct DkdvSrc {
+  __amdgpu_buffer_rsrc_t q, dout, lse2, dsum;
+};
+
+template <int D, int BQ>
+__device__ __forceinline__ void dkdv_load_stage(const DkdvSrc& src, int qb, int st, int w,
+                                                int lane, uint16_t* tq, float* sd) {
+  constexpr int HR = 64, HPB = BQ / HR;
+  const int row0 = qb * BQ + HR * (st % HPB);
+  tile_load_lds_rsrc<D, HR, 8>(src.q, row0, tq);
+  tile_load_lds_rsrc<D, HR, 8>(src.dout, row0, tq + HR * D);
+  if (w == 2 || w == 3)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(w == 2 ? src.lse2 : src.dsum,
+                                             (SPA_LDS void*)(sd + (w - 2) * HR), 4, lane * 4,
+                                             row0 * 4, 0, 0);
 }
 
-// P = exp2(S*scale*log2e - lse2) and dS = P (dP - D), in place; element e belongs to
-// query row r0 + acc_row(e, h) (two runs of 8 consecutive rows).
-__device__ __forceinline__ void slab_probs(const float* lse2s, const float* dss, int r0, int h,
-                                           float kmask, float scale_log2, f32x16& s,
-                                           f32x16& dp) {
+// Both jobs issue their LDS reads in batches ahead of the MFMAs that consume them
+// (sched_barrier fences keep the compiler from interleaving each read with its MFMA, which
+// would expose the LDS latency once per k-step).
+#define SPA_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Producer job on one staged 64-row slot: S, P (to LDS for the consumer), dV += P^T dO.
+template <int D>
+__device__ __forceinline__ void dkdv_producer(const uint16_t* tq, const float* sd, float* pw,
+                                              const bf16x8 (&kf)[D / 16], f32x16 (&acc)[D / 32],
+                                              int r0, int lane, bool tail, float kmask,
+                                              float scale_log2) {
+  constexpr int KS = D / 16, DB = D / 32, HR = 64;
+  const int h = lane >> 5;
+  const uint16_t* dOb = tq + HR * D;
+  bf16x8 a[KS], ob[2][DB];
+  float4 lv[4];
 #pragma unroll
-  for (int run = 0; run < 2; ++run) {
-    const int q0 = r0 + 16 * run + 8 * h;
-    const float4 l0 = *reinterpret_cast<const float4*>(lse2s + q0);
-    const float4 l1 = *reinterpret_cast<const float4*>(lse2s + q0 + 4);
-    const float4 d0 = *reinterpret_cast<const float4*>(dss + q0);
-    const float4 d1 = *reinterpret_cast<const float4*>(dss + q0 + 4);
-    const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-    const float dv_[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+  for (int kk = 0; kk < KS; ++kk) a[kk] = lds_rowfrag<D>(tq, r0, kk, lane);
+  // element e is query row r0 + acc_row(e, h): runs of 4 consecutive rows
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = 8 * run + u;
-      const float pe = kmask * __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -lv[u]));
-      s[e] = pe;
-      dp[e] = pe * (dp[e] - dv_[u]);
+  for (int g = 0; g < 4; ++g)
+    lv[g] = *reinterpret_cast<const float4*>(sd + r0 + 16 * (g >> 1) + 8 * h + 4 * (g & 1));
+#pragma unroll
+  for (int db = 0; db < DB; ++db) ob[0][db] = lds_colfrag<D>(dOb, r0, 32 * db, lane);
+  SPA_FENCE();
+  f32x16 sacc = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) sacc = mfma32(a[kk], kf[kk], sacc);
+  SPA_FENCE();
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    sacc[4 * g + 0] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + 0], scale_log2, -lv[g].x));
+    sacc[4 * g + 1] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + 1], scale_log2, -lv[g].y));
+    sacc[4 * g + 2] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + 2], scale_log2, -lv[g].z));
+    sacc[4 * g + 3] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + 3], scale_log2, -lv[g].w));
+  }
+  if (tail) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] *= kmask;
+  }
+  // P to the consumer of this unit: lane-contiguous float4 groups
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<float4*>(pw + (g * 64 + lane) * 4) =
+        make_float4(sacc[4 * g], sacc[4 * g + 1], sacc[4 * g + 2], sacc[4 * g + 3]);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) ob[1][db] = lds_colfrag<D>(dOb, r0 + 16, 32 * db, lane);
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq) {
+    bf16x8 ph, pl;
+    split_bf16x8(sacc, kq, ph, pl);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = mfma32(ph, ob[kq][db], acc[db]);
+      acc[db] = mfma32(pl, ob[kq][db], acc[db]);
     }
   }
 }
 
-// dV += P^T dO and dK += dS^T Q for the slab (P, dS as bf16 hi + lo pairs; dO^T, Q^T
-// gathered with transpose reads).
+// Consumer job on the previous stage's slot: dP, dS = P (dP - D), dK += dS^T Q.
 template <int D>
-__device__ __forceinline__ void slab_grads(const uint16_t* Qb, const uint16_t* dOb, int r0,
-                                           int lane, const f32x16& p, const f32x16& ds,
-                                           f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
+__device__ __forceinline__ void dkdv_consumer(const uint16_t* tq, const float* sd, const float* pr,
+                                              const bf16x8 (&vf)[D / 16], f32x16 (&acc)[D / 32],
+                                              int r0, int lane) {
+  constexpr int KS = D / 16, DB = D / 32, HR = 64;
+  const int h = lane >> 5;
+  const uint16_t* dOb = tq + HR * D;
+  bf16x8 a[KS], qb[2][DB];
+  float4 pv[4], dv4[4];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) a[kk] = lds_rowfrag<D>(dOb, r0, kk, lane);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    pv[g] = *reinterpret_cast<const float4*>(pr + (g * 64 + lane) * 4);
+    dv4[g] = *reinterpret_cast<const float4*>(sd + HR + r0 + 16 * (g >> 1) + 8 * h + 4 * (g & 1));
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db) qb[0][db] = lds_colfrag<D>(tq, r0, 32 * db, lane);
+  SPA_FENCE();
+  f32x16 dp = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) dp = mfma32(a[kk], vf[kk], dp);
+  SPA_FENCE();
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    dp[4 * g + 0] = pv[g].x * (dp[4 * g + 0] - dv4[g].x);
+    dp[4 * g + 1] = pv[g].y * (dp[4 * g + 1] - dv4[g].y);
+    dp[4 * g + 2] = pv[g].z * (dp[4 * g + 2] - dv4[g].z);
+    dp[4 * g + 3] = pv[g].w * (dp[4 * g + 3] - dv4[g].w);
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db) qb[1][db] = lds_colfrag<D>(tq, r0 + 16, 32 * db, lane);
 #pragma unroll
   for (int kq = 0; kq < 2; ++kq) {
-    bf16x8 ph, pl, dh, dl;
-    split_bf16x8(p, kq, ph, pl);
-    split_bf16x8(ds, kq, dh, dl);
+    bf16x8 dh, dl;
+    split_bf16x8(dp, kq, dh, dl);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const bf16x8 ob = lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
-      dva[db] = mfma32(ph, ob, dva[db]);
-      dva[db] = mfma32(pl, ob, dva[db]);
-      const bf16x8 qb = lds_colfrag<D>(Qb, r0 + 16 * kq, 32 * db, lane);
-      dka[db] = mfma32(dh, qb, dka[db]);
-      dka[db] = mfma32(dl, qb, dka[db]);
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = mfma32(dh, qb[kq][db], acc[db]);
+      acc[db] = mfma32(dl, qb[kq][db], acc[db]);
     }
   }
 }
 
 template <int D, int BQ>
-__global__ __launch_bounds__(256, 1) void k_dkdv(
+__global__ __launch_bounds__(512, 1) void k_dkdv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ dsum,
-    const int32_t* __restrict__ q_idx, const int32_t* __restrict__ q_cnt, int N, int nqb,
-    int nkb, int total, float scale_log2, float scale, void* __restrict__ dk_out,
+    const float* __restrict__ lse2p, const float* __restrict__ dsum,
+    const int32_t* __restrict__ q_idx, const int32_t* __restrict__ q_cnt, int N, int npad,
+    int nqb, int nkb, int total, float scale_log2, float scale, void* __restrict__ dk_out,
     void* __restrict__ dv_out, int grad_bf16) {
-  constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int SLABS = BQ / 32;          // 32-row slabs per query block
-  constexpr int TILE = BQ * D;            // elements of one staged Q or dO tile
-  constexpr int STAGE_BYTES = 2 * (2 * TILE * 2 + 2 * BQ * 4);  // 2 buffers: Q, dO, lse2, D
-  constexpr int RED_BYTES = 2 * 2 * 64 * DB * 16 * 4;           // dK, dV partials
-  constexpr int SMEM = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
-  __shared__ __align__(16) unsigned char smem[SMEM];
-  uint16_t* tiles = reinterpret_cast<uint16_t*>(smem);           // [buf][Q | dO][TILE]
-  float* side = reinterpret_cast<float*>(smem + 2 * 2 * TILE * 2);  // [buf][lse2 | D][BQ], 16-byte aligned
+  constexpr int KS = D / 16;
+  constexpr int HR = 64;                 // query rows per stage
+  constexpr int HPB = BQ / HR;           // stages per query block
+  constexpr int SLOT = 2 * HR * D;       // Q | dO of one stage
+  // Ring of three slots, each its own LDS object: the compiler can then tell the direct
+  // loads into one slot from the reads of the others and need not wait for the former.
+  __shared__ __align__(16) uint16_t tq0[SLOT], tq1[SLOT], tq2[SLOT];
+  __shared__ __align__(16) float sd0[2 * HR], sd1[2 * HR], sd2[2 * HR];  // [lse2 | D]
+  __shared__ __align__(16) float pb0[4 * 1024], pb1[4 * 1024], pb2[4 * 1024];  // [unit][32x32]
+  // the query-block list, staged once: reading it from LDS keeps scalar loads (which
+  // complete out of order) out of the loop, so LDS waits can stay partial
+  __shared__ int32_t lst[kMaxBlocks];
+  static_assert(2 * DB * 16 * 64 * 4 <= SLOT * 2, "reduction buffer reuses a slot");
 
   const int tile_id = xcd_remap(blockIdx.x, total);
   const int bh = tile_id / nkb;
   const int j = tile_id - bh * nkb;
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31, h = lane >> 5;
-  const int kh = wv & 1, par = wv >> 1;
+  const int role = w >> 2;               // 0 producer, 1 consumer
+  const int unit = w & 3;
+  const int kh = unit & 1, r0 = 32 * (unit >> 1);
   const size_t head = (size_t)bh * N * D;
   const int key = j * kBlkK + 32 * kh + c;  // this lane's key (B operand column)
-  const float kmask = key < N ? 1.f : 0.f;  // keys beyond N compute on a copy and get P = 0
+  const bool tail = j * kBlkK + kBlkK > N;  // keys at or beyond N exist only here
+  const float kmask = key < N ? 1.f : 0.f;
 
-  bf16x8 kf[KS], vf[KS];
+  bf16x8 bf[KS];  // producer: K row of this lane's key; consumer: V row
   {
-    const size_t krow = head + (size_t)min(key, N - 1) * D + 8 * h;
+    const uint16_t* src = (role ? v : k) + head + (size_t)min(key, N - 1) * D + 8 * h;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      kf[kk] = *reinterpret_cast<const bf16x8*>(k + krow + 16 * kk);
-      vf[kk] = *reinterpret_cast<const bf16x8*>(v + krow + 16 * kk);
-    }
+    for (int kk = 0; kk < KS; ++kk) bf[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
   }
-  f32x16 dka[DB], dva[DB];
+  f32x16 acc[DB];  // producer: dV; consumer: dK (unscaled)
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dka[db] = f32x16{};
-    dva[db] = f32x16{};
-  }
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
   const int32_t* list = q_idx + ((size_t)bh * nkb + j) * nqb;
-  const int cnt = q_cnt[(size_t)bh * nkb + j];
-  float lse_r = 0.f, d_r = 0.f;  // side values of row t (t < BQ) of the staged block
-  if (cnt > 0) {
-    const int r0 = list[0] * BQ;
-    tile_load_lds<D, BQ, 4>(q + head, r0, N, tiles);
-    tile_load_lds<D, BQ, 4>(dout + head, r0, N, tiles + TILE);
-    if (t < BQ) {
-      const int grow = r0 + t;
-      const size_t gi = (size_t)bh * N + min(grow, N - 1);
-      side[t] = grow < N ? lse[gi] * kLog2e : INFINITY;  // rows beyond N get P = 0
-      side[BQ + t] = grow < N ? dsum[gi] : 0.f;
-    }
-    wait_vmem();
-  }
-  __syncthreads();
-  for (int it = 0; it < cnt; ++it) {
-    const int b = it & 1;
-    {  // next query block (the last iteration reloads its own block; the copy goes unused)
-      const int r0 = list[min(it + 1, cnt - 1)] * BQ;
-      uint16_t* nb = tiles + (b ^ 1) * 2 * TILE;
-      tile_load_lds<D, BQ, 4>(q + head, r0, N, nb);
-      tile_load_lds<D, BQ, 4>(dout + head, r0, N, nb + TILE);
-      if (t < BQ) {
-        const int grow = r0 + t;
-        const size_t gi = (size_t)bh * N + min(grow, N - 1);
-        lse_r = grow < N ? lse[gi] * kLog2e : INFINITY;
-        d_r = grow < N ? dsum[gi] : 0.f;
-      }
-    }
-    const uint16_t* Qb = tiles + b * 2 * TILE;
-    const uint16_t* dOb = Qb + TILE;
-    const float* lse2s = side + b * 2 * BQ;
-    const float* dss = lse2s + BQ;
-    if constexpr (SLABS == 4) {
-      // two independent slabs per wave, software-pipelined: the MFMAs of one slab are
-      // issued next to the VALU work of the other
-      const int ra = 32 * par, rb = 32 * (par + 2);
-      f32x16 sa, dpa, sb, dpb;
-      slab_scores<D>(Qb, dOb, ra, kf, vf, lane, sa, dpa);
-      slab_scores<D>(Qb, dOb, rb, kf, vf, lane, sb, dpb);
-      slab_probs(lse2s, dss, ra, h, kmask, scale_log2, sa, dpa);
-      slab_grads<D>(Qb, dOb, ra, lane, sa, dpa, dka, dva);
-      slab_probs(lse2s, dss, rb, h, kmask, scale_log2, sb, dpb);
-      slab_grads<D>(Qb, dOb, rb, lane, sb, dpb, dka, dva);
-    } else {
-      const int ra = 32 * par;
-      f32x16 sa, dpa;
-      slab_scores<D>(Qb, dOb, ra, kf, vf, lane, sa, dpa);
-      slab_probs(lse2s, dss, ra, h, kmask, scale_log2, sa, dpa);
-      slab_grads<D>(Qb, dOb, ra, lane, sa, dpa, dka, dva);
-    }
-    if (t < BQ) {
-      side[(b ^ 1) * 2 * BQ + t] = lse_r;
-      side[(b ^ 1) * 2 * BQ + BQ + t] = d_r;
-    }
-    wait_vmem();
-    __syncthreads();
-  }
+  const int nst = q_cnt[(size_t)bh * nkb + j] * HPB;
+  DkdvSrc src;
+  src.q = make_rsrc(q + head, (uint32_t)N * D * 2);
+  src.dout = make_rsrc(dout + head, (uint32_t)N * D * 2);
+  src.lse2 = make_rsrc(lse2p + (size_t)bh * npad, (uint32_t)npad * 4);
+  src.dsum = make_rsrc(dsum + (size_t)bh * npad, (uint32_t)npad * 4);
 
-  // ---- reduce the two slab parities and write ------------------------------------------
-  float* red = reinterpret_cast<float*>(smem);  // [kh][K|V][DB*16][lane]: lane-contiguous
-  auto slot = [&](int which, int idx) { return ((kh * 2 + which) * (DB * 16) + idx) * 64 + lane; };
-  if (par == 1) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        red[slot(0, db * 16 + e)] = dka[db][e];
-        red[slot(1, db * 16 + e)] = dva[db][e];
-      }
+  // Query block of stage st + 1, read one step ahead so that the scalar load's latency
+  // is hidden behind a step of work.
+  const int cnt = nst / HPB;
+  for (int x = threadIdx.x; x < cnt; x += 512) lst[x] = list[x];
+  __syncthreads();
+  auto list_at = [&](int st) {
+    return __builtin_amdgcn_readfirstlane(lst[max(0, min(st / HPB, cnt - 1))]);
+  };
+  int qb_next = list_at(1);
+  if (nst > 0) {
+    dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tq0, sd0);
+    wait_vmem();
   }
   __syncthreads();
-  if (par == 0) {
+  // One step: loads of stage st+1 into slot N, producer on stage st (slot C), consumer on
+  // stage st-1 (slot P).  Three steps rotate the slots (C, P, N) = (0,2,1), (1,0,2),
+  // (2,1,0).  Each job has its own copy of the loop (same number of barriers).
+#define SPA_DKDV_LOAD(ST, TN, SN)                                                            \
+  {                                                                                        \
+    const int qb_ = qb_next;                                                               \
+    qb_next = list_at((ST) + 2);                                                           \
+    if ((ST) + 1 < nst)                                                                    \
+      dkdv_load_stage<D, BQ>(src, qb_, (ST) + 1, w, lane, TN, SN);                          \
+  }
+#define SPA_DKDV_PRODUCE(ST, TC, SC, PC, TP, SP, PP, TN, SN)                                 \
+  {                                                                                        \
+    SPA_DKDV_LOAD(ST, TN, SN)                                                              \
+    if ((ST) < nst)                                                                        \
+      dkdv_producer<D>(TC, SC, PC + unit * 1024, bf, acc, r0, lane, tail, kmask, scale_log2); \
+    wait_vmem();                                                                           \
+    __syncthreads();                                                                       \
+  }
+#define SPA_DKDV_CONSUME(ST, TC, SC, PC, TP, SP, PP, TN, SN)                                 \
+  {                                                                                        \
+    SPA_DKDV_LOAD(ST, TN, SN)                                                              \
+    if ((ST) >= 1) dkdv_consumer<D>(TP, SP, PP + unit * 1024, bf, acc, r0, lane);          \
+    wait_vmem();                                                                           \
+    __syncthreads();                                                                       \
+  }
+#define SPA_DKDV_LOOP(STEP)                                                                  \
+  for (int st = 0; st <= nst; st += 3) {                                                   \
+    STEP(st, tq0, sd0, pb0, tq2, sd2, pb2, tq1, sd1)                                       \
+    if (st + 1 > nst) break;                                                               \
+    STEP(st + 1, tq1, sd1, pb1, tq0, sd0, pb0, tq2, sd2)                                   \
+    if (st + 2 > nst) break;                                                               \
+    STEP(st + 2, tq2, sd2, pb2, tq1, sd1, pb1, tq0, sd0)                                   \
+  }
+  if (role == 0) {
+    SPA_DKDV_LOOP(SPA_DKDV_PRODUCE)
+  } else {
+    SPA_DKDV_LOOP(SPA_DKDV_CONSUME)
+  }
+#undef SPA_DKDV_LOOP
+#undef SPA_DKDV_CONSUME
+#undef SPA_DKDV_PRODUCE
+#undef SPA_DKDV_LOAD
+
+  // ---- add the two row slabs (fixed order) and write ------------------------------------
+  // [role][DB*16][lane], lane-contiguous; key half 0 in slot 0, key half 1 in slot 1
+  float* red = reinterpret_cast<float*>(kh ? tq1 : tq0);
+  const int rbase = role * (DB * 16);
+  if (r0 != 0) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[(rbase + db * 16 + e) * 64 + lane] = acc[db][e];
+  }
+  __syncthreads();
+  if (r0 == 0) {
+    void* out = role ? dk_out : dv_out;
+    const float f = role ? scale : 1.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float gk = (dka[db][e] + red[slot(0, db * 16 + e)]) * scale;
-        const float gv = dva[db][e] + red[slot(1, db * 16 + e)];
-        // accumulator element e: key row 8*(e/4) + 4*h + e%4 of this wave's 32 keys, column c
+        const float g = (acc[db][e] + red[(rbase + db * 16 + e) * 64 + lane]) * f;
+        // accumulator element e: key row 8*(e/4) + 4*h + e%4 of this unit's 32 keys, column c
         const int krow = j * kBlkK + 32 * kh + 8 * (e >> 2) + 4 * h + (e & 3);
         if (krow < N) {
           const size_t off = head + (size_t)krow * D + 32 * db + c;
-          if (grad_bf16) {
-            reinterpret_cast<__bf16*>(dk_out)[off] = (__bf16)gk;
-            reinterpret_cast<__bf16*>(dv_out)[off] = (__bf16)gv;
-          } else {
-            reinterpret_cast<float*>(dk_out)[off] = gk;
-            reinterpret_cast<float*>(dv_out)[off] = gv;
-          }
+          if (grad_bf16)
+            reinterpret_cast<__bf16*>(out)[off] = (__bf16)g;
+          else
+            reinterpret_cast<float*>(out)[off] = g;
         }
       }
   }
@@ -330,9 +413,9 @@ template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ dsum,
-    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int N, int nqb,
-    int nkb, int total, float scale_log2, float scale, void* __restrict__ dq_out,
+    const float* __restrict__ lse2p, const float* __restrict__ dsum,
+    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int N, int npad,
+    int nqb, int nkb, int total, float scale_log2, float scale, void* __restrict__ dq_out,
     int grad_bf16) {
   constexpr int NT = BQ * 2;
   constexpr int KS = D / 16;
@@ -359,8 +442,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     qf[kk] = *reinterpret_cast<const bf16x8*>(q + qoff + 16 * kk);
     df[kk] = *reinterpret_cast<const bf16x8*>(dout + qoff + 16 * kk);
   }
-  const size_t ri = (size_t)bh * N + min(qrow, N - 1);
-  const float lse2 = lse[ri] * kLog2e;
+  const size_t ri = (size_t)bh * npad + qrow;  // padded side arrays: rows beyond N hold P = 0
+  const float lse2 = lse2p[ri];
   const float dq_sum = dsum[ri];
 
   f32x16 acc[DB];
@@ -446,9 +529,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
 // ------------------------------------------------------------------------------------
 static int n_words(const Geometry& g) { return (g.nkb + 31) / 32; }
 
+static size_t n_pad(const Geometry& g) { return (size_t)g.nqb * g.blk_q; }
+
 size_t bwd_workspace_bytes(const Geometry& g) {
   const size_t bh = (size_t)g.bh();
-  return align_up(bh * g.N * sizeof(float), 256) +
+  return 2 * align_up(bh * n_pad(g) * sizeof(float), 256) +
          align_up(bh * n_words(g) * g.nqb * sizeof(uint32_t), 256) +
          align_up(bh * g.nkb * g.nqb * sizeof(int32_t), 256) +
          align_up(bh * g.nkb * sizeof(int32_t), 256);
@@ -458,7 +543,9 @@ void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a) {
   const size_t bh = (size_t)g.bh();
   char* p = static_cast<char*>(ws);
   a->dsum = reinterpret_cast<float*>(p);
-  p += align_up(bh * g.N * sizeof(float), 256);
+  p += align_up(bh * n_pad(g) * sizeof(float), 256);
+  a->lse2 = reinterpret_cast<float*>(p);
+  p += align_up(bh * n_pad(g) * sizeof(float), 256);
   a->bits = reinterpret_cast<uint32_t*>(p);
   p += align_up(bh * n_words(g) * g.nqb * sizeof(uint32_t), 256);
   a->q_idx = reinterpret_cast<int32_t*>(p);
@@ -470,11 +557,12 @@ template <int D, int BQ>
 static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s) {
   const Geometry& g = a.g;
   const float sl2 = a.scale * kLog2e;
+  const int npad = (int)n_pad(g);
   if (stages & 1u) {
-    const long long rows = (long long)g.bh() * g.N;
+    const long long rows = (long long)g.bh() * npad;
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((k_dsum<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s,
-                       a.o, a.o_lo, a.dout, rows, a.dsum);
+                       a.o, a.o_lo, a.dout, a.lse, g.N, npad, rows, a.dsum, a.lse2);
     const int nw = n_words(g);
     hipLaunchKernelGGL(k_bitmap, dim3(g.nqb, (unsigned)g.bh()), dim3(64), 0, s, a.kv_idx,
                        a.kv_cnt, g.nqb, g.nkb, nw, a.bits);
@@ -483,15 +571,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
   }
   if (stages & 2u) {
     const int total = (int)(g.nkb * g.bh());
-    hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(total), dim3(256), 0, s, a.q, a.k, a.v, a.dout,
-                       a.lse, a.dsum, a.q_idx, a.q_cnt, g.N, g.nqb, g.nkb, total, sl2, a.scale,
-                       a.dk, a.dv, a.grad_bf16);
+    hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(total), dim3(512), 0, s, a.q, a.k, a.v, a.dout,
+                       a.lse2, a.dsum, a.q_idx, a.q_cnt, g.N, npad, g.nqb, g.nkb, total, sl2,
+                       a.scale, a.dk, a.dv, a.grad_bf16);
   }
   if (stages & 4u) {
     const int total = (int)(g.nqb * g.bh());
     hipLaunchKernelGGL((k_dq<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.dout,
-                       a.lse, a.dsum, a.kv_idx, a.kv_cnt, g.N, g.nqb, g.nkb, total, sl2, a.scale,
-                       a.dq, a.grad_bf16);
+                       a.lse2, a.dsum, a.kv_idx, a.kv_cnt, g.N, npad, g.nqb, g.nkb, total, sl2,
+                       a.scale, a.dq, a.grad_bf16);
   }
   return hipGetLastError();
 }

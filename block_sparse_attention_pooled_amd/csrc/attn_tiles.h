@@ -80,6 +80,34 @@ __device__ __forceinline__ void tile_load_lds(const uint16_t* __restrict__ base,
   }
 }
 
+// Raw buffer resource over [base, base + bytes): loads beyond the range return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// The same tile staging through a buffer resource over one head's [N, D] matrix: the
+// per-lane offsets are loop invariant (the tile's first row enters as a scalar offset), and
+// rows at or beyond N read as zeros (the range check of the resource) instead of being
+// clamped.
+template <int D, int NROWS, int NWAVES>
+__device__ __forceinline__ void tile_load_lds_rsrc(__amdgpu_buffer_rsrc_t rsrc, int row0,
+                                                   uint16_t* lds) {
+  constexpr int SEGS = NROWS * D * 2 / 1024;
+  constexpr int PER = SEGS / NWAVES;
+  constexpr int RPS = 1024 / (D * 2);
+  static_assert(SEGS % NWAVES == 0, "segments must divide among the waves");
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int seg = wv * PER + u;
+    const int row = seg * RPS + lane / Tile<D>::CPR;
+    const int cc = (lane % Tile<D>::CPR) ^ Tile<D>::swz(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (SPA_LDS void*)(lds + seg * 512), 16,
+                                             (row * D + cc * 8) * 2, row0 * D * 2, 0, 0);
+  }
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // A (or B) operand holding X[r0 + perm32(c)][16*kk + 8*h .. +7] for lane c + 32*h.

@@ -11,7 +11,7 @@ namespace {
 
 using spa::Geometry;
 
-constexpr int kMaxKeyBlocks = 2048;
+constexpr int kMaxKeyBlocks = 2048;  // kMaxBlocks of the kernels
 
 int check_dims(const spa_dims* d, Geometry* g) {
   if (!d) return SPA_E_NULL;

@@ -17,6 +17,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 
 constexpr int kWave = 64;
 constexpr int kBlkK = 64;  // key block size
+constexpr int kMaxBlocks = 2048;  // most key blocks per head (query blocks are never more)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -124,7 +124,8 @@ SPA_API int spa_sparse_attn_fwd(const spa_dims* dims, const void* q, const void*
                         const int32_t* kv_idx, const int32_t* kv_cnt, double scale, void* o,
                         void* o_lo, float* lse, void* stream);
 
-/* Bytes of device workspace spa_sparse_attn_bwd needs (D = rowsum(dO*O), the kept-tile
+/* Bytes of device workspace spa_sparse_attn_bwd needs (D = rowsum(dO*O) and lse*log2(e)
+ * per row, padded to whole query blocks, the kept-tile
  * bitmap and the per-key-block query-block lists).  0 for rejected dims. */
 SPA_API size_t spa_bwd_workspace_bytes(const spa_dims* dims);
 
