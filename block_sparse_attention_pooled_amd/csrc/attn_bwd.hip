@@ -124,26 +124,26 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
 // dK, dV: one workgroup per key block (workgroups in XCD-contiguous order), 8 wavefronts,
 // one workgroup per CU.  The key block's query-block list is walked in stages of 64 query
 // rows; Q and dO of each stage stream into a ring of three LDS slots with direct
-// global->LDS loads, two stages ahead of their last use.
+// buffer->LDS loads, one stage ahead.
 //
 // The 64 keys x 64 rows of a stage split into four units (32 keys x 32 rows).  Each
 // unit has two wavefronts with different jobs, placed so that they share a SIMD:
 //   producer (waves 0-3):  S = Q K^T (K fragments in registers), P = exp2(S c - lse2),
 //                          P to LDS (fp32), dV += P^T dO with P as a bf16 hi + lo pair;
-//   consumer (waves 4-7):  one stage behind, dP = dO V^T (V fragments in registers),
+//   consumer (waves 4-7):  one stage behind: dP = dO V^T (V fragments in registers),
 //                          P from LDS, dS = P (dP - D), dK += dS^T Q with dS as a bf16
 //                          hi + lo pair.
 // The two jobs of a SIMD interleave freely (one wavefront's exp and conversions run
 // while the other's MFMAs execute).  Each wavefront's partial sums cover its 32-row
 // slab of every stage; the two slabs are added at the end in a fixed order.
 // ------------------------------------------------------------------------------------
-// Loads of stage st (64 query rows of query block qb) into one ring slot: the Q and dO
-// tiles and the lse2 / D rows (one 4-byte direct load per lane).  Q and dO rows at or
-// beyond N read as zeros; their lse2 of +inf makes their P exactly 0.
 struct DkdvSrc {
-  __amdgpu_buffer_rsrc_t q, dout, lse2, dsum;
+  u32x4 q, dout, lse2, dsum;
 };
 
+// Loads of stage st (64 query rows of query block qb) into one ring slot: the Q and dO
+// tiles and the lse2 / D rows (one 4-byte transfer per lane, waves 2 and 3).  Q and dO
+// rows at or beyond N read as zeros; their lse2 of +inf makes their P exactly 0.
 template <int D, int BQ>
 __device__ __forceinline__ void dkdv_load_stage(const DkdvSrc& src, int qb, int st, int w,
                                                 int lane, uint16_t* tq, float* sd) {
@@ -151,10 +151,8 @@ __device__ __forceinline__ void dkdv_load_stage(const DkdvSrc& src, int qb, int 
   const int row0 = qb * BQ + HR * (st % HPB);
   tile_load_lds_rsrc<D, HR, 8>(src.q, row0, tq);
   tile_load_lds_rsrc<D, HR, 8>(src.dout, row0, tq + HR * D);
-  if (w == 2 || w == 3)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(w == 2 ? src.lse2 : src.dsum,
-                                             (SPA_LDS void*)(sd + (w - 2) * HR), 4, lane * 4,
-                                             row0 * 4, 0, 0);
+  if (w == 2) dma4(src.lse2, lane * 4, row0 * 4, lds_addr(sd));
+  if (w == 3) dma4(src.dsum, lane * 4, row0 * 4, lds_addr(sd + HR));
 }
 
 // Both jobs issue their LDS reads in batches ahead of the MFMAs that consume them
@@ -162,16 +160,15 @@ __device__ __forceinline__ void dkdv_load_stage(const DkdvSrc& src, int qb, int 
 // would expose the LDS latency once per k-step).
 #define SPA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// Producer job on one staged 64-row slot: S, P (to LDS for the consumer), dV += P^T dO.
+// Producer, first half: S and P for the unit; P goes to LDS for the consumer.
 template <int D>
-__device__ __forceinline__ void dkdv_producer(const uint16_t* tq, const float* sd, float* pw,
-                                              const bf16x8 (&kf)[D / 16], f32x16 (&acc)[D / 32],
-                                              int r0, int lane, bool tail, float kmask,
-                                              float scale_log2) {
-  constexpr int KS = D / 16, DB = D / 32, HR = 64;
+__device__ __forceinline__ void dkdv_scores(const uint16_t* tq, const float* sd, float* pw,
+                                            const bf16x8 (&kf)[D / 16], int r0, int lane,
+                                            bool tail, float kmask, float scale_log2,
+                                            f32x16& sacc) {
+  constexpr int KS = D / 16;
   const int h = lane >> 5;
-  const uint16_t* dOb = tq + HR * D;
-  bf16x8 a[KS], ob[2][DB];
+  bf16x8 a[KS];
   float4 lv[4];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) a[kk] = lds_rowfrag<D>(tq, r0, kk, lane);
@@ -179,10 +176,8 @@ __device__ __forceinline__ void dkdv_producer(const uint16_t* tq, const float* s
 #pragma unroll
   for (int g = 0; g < 4; ++g)
     lv[g] = *reinterpret_cast<const float4*>(sd + r0 + 16 * (g >> 1) + 8 * h + 4 * (g & 1));
-#pragma unroll
-  for (int db = 0; db < DB; ++db) ob[0][db] = lds_colfrag<D>(dOb, r0, 32 * db, lane);
   SPA_FENCE();
-  f32x16 sacc = f32x16{};
+  sacc = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) sacc = mfma32(a[kk], kf[kk], sacc);
   SPA_FENCE();
@@ -197,48 +192,65 @@ __device__ __forceinline__ void dkdv_producer(const uint16_t* tq, const float* s
 #pragma unroll
     for (int e = 0; e < 16; ++e) sacc[e] *= kmask;
   }
-  // P to the consumer of this unit: lane-contiguous float4 groups
+  // lane-contiguous float4 groups: the consumer lane with the same index reads them back
 #pragma unroll
   for (int g = 0; g < 4; ++g)
     *reinterpret_cast<float4*>(pw + (g * 64 + lane) * 4) =
         make_float4(sacc[4 * g], sacc[4 * g + 1], sacc[4 * g + 2], sacc[4 * g + 3]);
-#pragma unroll
-  for (int db = 0; db < DB; ++db) ob[1][db] = lds_colfrag<D>(dOb, r0 + 16, 32 * db, lane);
+}
+
+// Producer, second half: dV += P^T dO.
+template <int D>
+__device__ __forceinline__ void dkdv_dv(const uint16_t* tq, const f32x16& p, f32x16 (&acc)[D / 32],
+                                        int r0, int lane) {
+  constexpr int DB = D / 32, HR = 64;
+  const uint16_t* dOb = tq + HR * D;
 #pragma unroll
   for (int kq = 0; kq < 2; ++kq) {
+    bf16x8 ob[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) ob[db] = lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
     bf16x8 ph, pl;
-    split_bf16x8(sacc, kq, ph, pl);
+    split_bf16x8(p, kq, ph, pl);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      acc[db] = mfma32(ph, ob[kq][db], acc[db]);
-      acc[db] = mfma32(pl, ob[kq][db], acc[db]);
+      acc[db] = mfma32(ph, ob[db], acc[db]);
+      acc[db] = mfma32(pl, ob[db], acc[db]);
     }
   }
 }
 
-// Consumer job on the previous stage's slot: dP, dS = P (dP - D), dK += dS^T Q.
+// Consumer, first half: dP for the unit.
 template <int D>
-__device__ __forceinline__ void dkdv_consumer(const uint16_t* tq, const float* sd, const float* pr,
-                                              const bf16x8 (&vf)[D / 16], f32x16 (&acc)[D / 32],
-                                              int r0, int lane) {
-  constexpr int KS = D / 16, DB = D / 32, HR = 64;
-  const int h = lane >> 5;
+__device__ __forceinline__ void dkdv_dp(const uint16_t* tq, const bf16x8 (&vf)[D / 16], int r0,
+                                        int lane, f32x16& dp) {
+  constexpr int KS = D / 16, HR = 64;
   const uint16_t* dOb = tq + HR * D;
-  bf16x8 a[KS], qb[2][DB];
-  float4 pv[4], dv4[4];
+  bf16x8 a[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) a[kk] = lds_rowfrag<D>(dOb, r0, kk, lane);
+  SPA_FENCE();
+  dp = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) dp = mfma32(a[kk], vf[kk], dp);
+}
+
+// Consumer, second half: dS = P (dP - D) with P from the producer, dK += dS^T Q.
+template <int D>
+__device__ __forceinline__ void dkdv_dk(const uint16_t* tq, const float* sd, const float* pr,
+                                        f32x16& dp, f32x16 (&acc)[D / 32], int r0, int lane) {
+  constexpr int DB = D / 32, HR = 64;
+  const int h = lane >> 5;
+  const float* dsv = sd + HR;
+  float4 pv[4], dv4[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     pv[g] = *reinterpret_cast<const float4*>(pr + (g * 64 + lane) * 4);
-    dv4[g] = *reinterpret_cast<const float4*>(sd + HR + r0 + 16 * (g >> 1) + 8 * h + 4 * (g & 1));
+    dv4[g] = *reinterpret_cast<const float4*>(dsv + r0 + 16 * (g >> 1) + 8 * h + 4 * (g & 1));
   }
+  bf16x8 qb[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) qb[0][db] = lds_colfrag<D>(tq, r0, 32 * db, lane);
-  SPA_FENCE();
-  f32x16 dp = f32x16{};
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) dp = mfma32(a[kk], vf[kk], dp);
+  for (int db = 0; db < DB; ++db) qb[db] = lds_colfrag<D>(tq, r0, 32 * db, lane);
   SPA_FENCE();
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -248,15 +260,17 @@ __device__ __forceinline__ void dkdv_consumer(const uint16_t* tq, const float* s
     dp[4 * g + 3] = pv[g].w * (dp[4 * g + 3] - dv4[g].w);
   }
 #pragma unroll
-  for (int db = 0; db < DB; ++db) qb[1][db] = lds_colfrag<D>(tq, r0 + 16, 32 * db, lane);
-#pragma unroll
   for (int kq = 0; kq < 2; ++kq) {
+    if (kq == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) qb[db] = lds_colfrag<D>(tq, r0 + 16, 32 * db, lane);
+    }
     bf16x8 dh, dl;
     split_bf16x8(dp, kq, dh, dl);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      acc[db] = mfma32(dh, qb[kq][db], acc[db]);
-      acc[db] = mfma32(dl, qb[kq][db], acc[db]);
+      acc[db] = mfma32(dh, qb[db], acc[db]);
+      acc[db] = mfma32(dl, qb[db], acc[db]);
     }
   }
 }
@@ -274,11 +288,9 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   constexpr int HR = 64;                 // query rows per stage
   constexpr int HPB = BQ / HR;           // stages per query block
   constexpr int SLOT = 2 * HR * D;       // Q | dO of one stage
-  // Ring of three slots, each its own LDS object: the compiler can then tell the direct
-  // loads into one slot from the reads of the others and need not wait for the former.
-  __shared__ __align__(16) uint16_t tq0[SLOT], tq1[SLOT], tq2[SLOT];
-  __shared__ __align__(16) float sd0[2 * HR], sd1[2 * HR], sd2[2 * HR];  // [lse2 | D]
-  __shared__ __align__(16) float pb0[4 * 1024], pb1[4 * 1024], pb2[4 * 1024];  // [unit][32x32]
+  __shared__ __align__(16) uint16_t tiles[3][SLOT];
+  __shared__ __align__(16) float side[3][2 * HR];     // [slot][lse2 | D]
+  __shared__ __align__(16) float pbuf[2][4 * 1024];   // [stage parity][unit][32x32] fp32
   // the query-block list, staged once: reading it from LDS keeps scalar loads (which
   // complete out of order) out of the loop, so LDS waits can stay partial
   __shared__ int32_t lst[kMaxBlocks];
@@ -298,84 +310,69 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   const bool tail = j * kBlkK + kBlkK > N;  // keys at or beyond N exist only here
   const float kmask = key < N ? 1.f : 0.f;
 
-  bf16x8 bf[KS];  // producer: K row of this lane's key; consumer: V row
-  {
-    const uint16_t* src = (role ? v : k) + head + (size_t)min(key, N - 1) * D + 8 * h;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) bf[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
-  }
-  f32x16 acc[DB];  // producer: dV; consumer: dK (unscaled)
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-
   const int32_t* list = q_idx + ((size_t)bh * nkb + j) * nqb;
-  const int nst = q_cnt[(size_t)bh * nkb + j] * HPB;
+  const int cnt = q_cnt[(size_t)bh * nkb + j];
+  const int nst = cnt * HPB;
   DkdvSrc src;
   src.q = make_rsrc(q + head, (uint32_t)N * D * 2);
   src.dout = make_rsrc(dout + head, (uint32_t)N * D * 2);
   src.lse2 = make_rsrc(lse2p + (size_t)bh * npad, (uint32_t)npad * 4);
   src.dsum = make_rsrc(dsum + (size_t)bh * npad, (uint32_t)npad * 4);
-
-  // Query block of stage st + 1, read one step ahead so that the scalar load's latency
-  // is hidden behind a step of work.
-  const int cnt = nst / HPB;
   for (int x = threadIdx.x; x < cnt; x += 512) lst[x] = list[x];
   __syncthreads();
   auto list_at = [&](int st) {
     return __builtin_amdgcn_readfirstlane(lst[max(0, min(st / HPB, cnt - 1))]);
   };
-  int qb_next = list_at(1);
-  if (nst > 0) {
-    dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tq0, sd0);
-    wait_vmem();
+  if (nst > 0) dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tiles[0], side[0]);
+
+  bf16x8 bf[KS];  // producer: K row of this lane's key; consumer: V row
+  {
+    const uint16_t* src_row = (role ? v : k) + head + (size_t)min(key, N - 1) * D + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) bf[kk] = *reinterpret_cast<const bf16x8*>(src_row + 16 * kk);
   }
+  f32x16 acc[DB];  // producer: dV; consumer: dK (unscaled)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  wait_vmem();  // stage 0 and the K / V fragments: nothing of the compiler's is pending
   __syncthreads();
-  // One step: loads of stage st+1 into slot N, producer on stage st (slot C), consumer on
-  // stage st-1 (slot P).  Three steps rotate the slots (C, P, N) = (0,2,1), (1,0,2),
-  // (2,1,0).  Each job has its own copy of the loop (same number of barriers).
-#define SPA_DKDV_LOAD(ST, TN, SN)                                                            \
+
+  // One step: loads of stage st+1 into the next slot, producer on stage st, consumer on
+  // stage st-1.  Each job runs its own copy of the loop (same barriers), so that neither
+  // keeps the other's loop-invariant addresses alive.
+#define SPA_DKDV_LOOP(JOB)                                                                   \
   {                                                                                        \
-    const int qb_ = qb_next;                                                               \
-    qb_next = list_at((ST) + 2);                                                           \
-    if ((ST) + 1 < nst)                                                                    \
-      dkdv_load_stage<D, BQ>(src, qb_, (ST) + 1, w, lane, TN, SN);                          \
-  }
-#define SPA_DKDV_PRODUCE(ST, TC, SC, PC, TP, SP, PP, TN, SN)                                 \
-  {                                                                                        \
-    SPA_DKDV_LOAD(ST, TN, SN)                                                              \
-    if ((ST) < nst)                                                                        \
-      dkdv_producer<D>(TC, SC, PC + unit * 1024, bf, acc, r0, lane, tail, kmask, scale_log2); \
-    wait_vmem();                                                                           \
-    __syncthreads();                                                                       \
-  }
-#define SPA_DKDV_CONSUME(ST, TC, SC, PC, TP, SP, PP, TN, SN)                                 \
-  {                                                                                        \
-    SPA_DKDV_LOAD(ST, TN, SN)                                                              \
-    if ((ST) >= 1) dkdv_consumer<D>(TP, SP, PP + unit * 1024, bf, acc, r0, lane);          \
-    wait_vmem();                                                                           \
-    __syncthreads();                                                                       \
-  }
-#define SPA_DKDV_LOOP(STEP)                                                                  \
-  for (int st = 0; st <= nst; st += 3) {                                                   \
-    STEP(st, tq0, sd0, pb0, tq2, sd2, pb2, tq1, sd1)                                       \
-    if (st + 1 > nst) break;                                                               \
-    STEP(st + 1, tq1, sd1, pb1, tq0, sd0, pb0, tq2, sd2)                                   \
-    if (st + 2 > nst) break;                                                               \
-    STEP(st + 2, tq2, sd2, pb2, tq1, sd1, pb1, tq0, sd0)                                   \
+    int cur = 0, prev = 2;                                                                 \
+    for (int st = 0; st <= nst; ++st) {                                                    \
+      const int nxt = cur == 2 ? 0 : cur + 1;                                              \
+      if (st + 1 < nst)                                                                    \
+        dkdv_load_stage<D, BQ>(src, list_at(st + 1), st + 1, w, lane, tiles[nxt], side[nxt]); \
+      JOB;                                                                                 \
+      wait_vmem();                                                                         \
+      __syncthreads();                                                                     \
+      prev = cur;                                                                          \
+      cur = nxt;                                                                           \
+    }                                                                                      \
   }
   if (role == 0) {
-    SPA_DKDV_LOOP(SPA_DKDV_PRODUCE)
+    SPA_DKDV_LOOP(if (st < nst) {
+      f32x16 p;
+      dkdv_scores<D>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane, tail,
+                     kmask, scale_log2, p);
+      dkdv_dv<D>(tiles[cur], p, acc, r0, lane);
+    })
   } else {
-    SPA_DKDV_LOOP(SPA_DKDV_CONSUME)
+    SPA_DKDV_LOOP(if (st >= 1) {
+      f32x16 dp;
+      dkdv_dp<D>(tiles[prev], bf, r0, lane, dp);
+      dkdv_dk<D>(tiles[prev], side[prev], pbuf[(st - 1) & 1] + unit * 1024, dp, acc, r0, lane);
+    })
   }
 #undef SPA_DKDV_LOOP
-#undef SPA_DKDV_CONSUME
-#undef SPA_DKDV_PRODUCE
-#undef SPA_DKDV_LOAD
 
   // ---- add the two row slabs (fixed order) and write ------------------------------------
   // [role][DB*16][lane], lane-contiguous; key half 0 in slot 0, key half 1 in slot 1
-  float* red = reinterpret_cast<float*>(kh ? tq1 : tq0);
+  float* red = reinterpret_cast<float*>(tiles[kh]);
   const int rbase = role * (DB * 16);
   if (r0 != 0) {
 #pragma unroll
@@ -421,6 +418,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   __shared__ __align__(16) uint16_t smem[2][2][Tile<D>::ELEMS];  // [buf][K|V]
+  __shared__ int32_t lst[kMaxBlocks];  // the key-block list (keeps scalar loads out of the loop)
 
   const int tile_id = xcd_remap(blockIdx.x, total);
   const int bh = tile_id / nqb;
@@ -428,10 +426,12 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c = lane & 31, h = lane >> 5;
   const size_t head = (size_t)bh * N * D;
-  const uint16_t* kh_ = k + head;
-  const uint16_t* vh_ = v + head;
+  const u32x4 krs = make_rsrc(k + head, (uint32_t)N * D * 2);
+  const u32x4 vrs = make_rsrc(v + head, (uint32_t)N * D * 2);
   const int32_t* list = kv_idx + ((size_t)bh * nqb + i) * nkb;
   const int cnt = kv_cnt[(size_t)bh * nqb + i];
+  for (int x = threadIdx.x; x < cnt; x += NT) lst[x] = list[x];
+  auto blk = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[min(t, cnt - 1)]); };
 
   const int qrow = i * BQ + 32 * wv + c;
   const bool qvalid = qrow < N;
@@ -450,21 +450,21 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
+  __syncthreads();  // list staged
   if (cnt > 0) {
-    const int j0 = list[0];
-    tile_load_lds<D, kBlkK, NT / 64>(kh_, j0 * kBlkK, N, smem[0][0]);
-    tile_load_lds<D, kBlkK, NT / 64>(vh_, j0 * kBlkK, N, smem[0][1]);
-    wait_vmem();
+    const int j0 = blk(0);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0]);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, j0 * kBlkK, smem[0][1]);
   }
+  wait_vmem();  // also the row fragments: nothing vector-memory is pending inside the loop
   __syncthreads();
   for (int t = 0; t < cnt; ++t) {
     const int buf = t & 1;
-    const int j = list[t];
-    {  // next tile streams into the other buffer (the last iteration reloads its own
-       // tile; the copy goes unused)
-      const int jn = list[min(t + 1, cnt - 1)];
-      tile_load_lds<D, kBlkK, NT / 64>(kh_, jn * kBlkK, N, smem[buf ^ 1][0]);
-      tile_load_lds<D, kBlkK, NT / 64>(vh_, jn * kBlkK, N, smem[buf ^ 1][1]);
+    const int j = blk(t);
+    if (t + 1 < cnt) {  // the next tile streams into the other buffer meanwhile
+      const int jn = blk(t + 1);
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0]);
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, jn * kBlkK, smem[buf ^ 1][1]);
     }
     const uint16_t* Ks = smem[buf][0];
     const uint16_t* Vs = smem[buf][1];

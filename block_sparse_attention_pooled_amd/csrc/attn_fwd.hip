@@ -6,8 +6,8 @@
 // One workgroup per (b, h, query block), one wavefront per 32 query rows, workgroups
 // ordered so that each XCD works on a contiguous run of query blocks of one head.  For
 // each listed key block (64 keys) the K and V tiles stream row-major into LDS with
-// direct global->LDS loads, double buffered: the next tile is in flight while the
-// current one is used.
+// direct buffer->LDS loads (rows beyond N arrive as zeros), double buffered: the next
+// tile is in flight while the current one is used.
 // Per wavefront and tile:
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16 (K rows read in perm32 order, Q in
 //                 registers), so every lane holds 32 scores of a single query row;
@@ -26,6 +26,91 @@
 namespace spa {
 
 
+#define SPA_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// One kept tile: S^T for this wave's 32 query rows, online softmax update, O^T += V^T P^T.
+// K and V rows at or beyond N were staged as zeros; their scores are masked here.
+template <int D, bool SPLIT>
+__device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs, int key0, int N,
+                                         const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
+                                         float& m_run, float& l_run, float scale_log2, int lane) {
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  const int h = lane >> 5;
+  // ---- S^T = K Q^T : two 32-key slabs, K fragments read in batches of four k-steps ------
+  f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int k0 = 0; k0 < KS; k0 += 4) {
+    bf16x8 a0[4], a1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a0[u] = lds_rowfrag<D>(Ks, 0, k0 + u, lane);
+      a1[u] = lds_rowfrag<D>(Ks, 32, k0 + u, lane);
+    }
+    SPA_FENCE();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sc[0] = mfma32(a0[u], qf[k0 + u], sc[0]);
+      sc[1] = mfma32(a1[u], qf[k0 + u], sc[1]);
+    }
+  }
+  // keys at or beyond N exist only in the last key block
+  if (key0 + kBlkK > N) {
+    const int lim = N - key0 - 8 * h;  // element e is valid iff acc_row(e,0) < lim
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = 16 * (e >> 3) + (e & 7);
+      if (r >= lim) sc[0][e] = -INFINITY;
+      if (r + 32 >= lim) sc[1][e] = -INFINITY;
+    }
+  }
+  // ---- online softmax (log2 domain, scale folded into the exponent) --------------------
+  float mloc = sc[0][0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sc[0][e]);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sc[1][e]);
+  mloc = fmaxf(mloc, swap_halves(mloc)) * scale_log2;
+  // With o_lo requested, P's rounding is carried by the lo half and the running maximum
+  // may lag the true one by up to 8 (log2 units).  Without it the maximum is exact, so the
+  // dominant probability of a peaked row is exactly 1 and rounds without error.
+  constexpr float kSlack = SPLIT ? 8.0f : 0.0f;
+  const bool raise = mloc > m_run + kSlack;
+  if (__ballot(raise)) {
+    const float m_new = raise ? mloc : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+  }
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    sc[0][e] = __builtin_amdgcn_exp2f(fmaf(sc[0][e], scale_log2, -m_run));
+    sc[1][e] = __builtin_amdgcn_exp2f(fmaf(sc[1][e], scale_log2, -m_run));
+    psum += sc[0][e] + sc[1][e];
+  }
+  l_run += psum;
+  // ---- O^T += V^T P^T ---------------------------------------------------------------
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    bf16x8 ph, pl;
+    if constexpr (SPLIT)
+      split_bf16x8(sc[kk >> 1], kk & 1, ph, pl);
+    else
+      ph = to_bf16x8(sc[kk >> 1], kk & 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 va = lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
+      oacc[db] = mfma32(va, ph, oacc[db]);
+      if constexpr (SPLIT) oacc[db] = mfma32(va, pl, oacc[db]);
+    }
+  }
+}
+
 template <int D, int BQ, bool SPLIT>
 __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ q,
                                                   const uint16_t* __restrict__ k,
@@ -40,6 +125,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   constexpr int KS = D / 16;  // k-steps over the head dimension
   constexpr int DB = D / 32;  // 32-wide column blocks of O
   __shared__ __align__(16) uint16_t smem[2][2][Tile<D>::ELEMS];  // [buf][K|V]
+  __shared__ int32_t lst[kMaxBlocks];  // the key-block list (keeps scalar loads out of the loop)
 
   const int tile_id = xcd_remap(blockIdx.x, total);
   const int bh = tile_id / nqb;
@@ -47,10 +133,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c = lane & 31, h = lane >> 5;
   const size_t head = (size_t)bh * N * D;
-  const uint16_t* kh_ = k + head;
-  const uint16_t* vh_ = v + head;
+  const u32x4 krs = make_rsrc(k + head, (uint32_t)N * D * 2);
+  const u32x4 vrs = make_rsrc(v + head, (uint32_t)N * D * 2);
   const int32_t* list = kv_idx + ((size_t)bh * nqb + i) * nkb;
   const int cnt = kv_cnt[(size_t)bh * nqb + i];
+  for (int x = threadIdx.x; x < cnt; x += NT) lst[x] = list[x];
 
   // this lane's query row (B operand of S^T = K Q^T); rows beyond N compute on a copy of
   // row N-1 and are never written
@@ -66,89 +153,24 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  __syncthreads();  // list staged
+  auto blk = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[min(t, cnt - 1)]); };
   if (cnt > 0) {
-    const int j0 = list[0];
-    tile_load_lds<D, kBlkK, NT / 64>(kh_, j0 * kBlkK, N, smem[0][0]);
-    tile_load_lds<D, kBlkK, NT / 64>(vh_, j0 * kBlkK, N, smem[0][1]);
-    wait_vmem();
+    const int j0 = blk(0);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0]);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, j0 * kBlkK, smem[0][1]);
   }
+  wait_vmem();  // also the Q fragments: nothing vector-memory is pending inside the loop
   __syncthreads();
-
   for (int t = 0; t < cnt; ++t) {
     const int buf = t & 1;
-    const int j = list[t];
-    {  // next tile streams into the other buffer (the last iteration reloads its own
-       // tile; the copy goes unused)
-      const int jn = list[min(t + 1, cnt - 1)];
-      tile_load_lds<D, kBlkK, NT / 64>(kh_, jn * kBlkK, N, smem[buf ^ 1][0]);
-      tile_load_lds<D, kBlkK, NT / 64>(vh_, jn * kBlkK, N, smem[buf ^ 1][1]);
+    if (t + 1 < cnt) {  // the next tile streams into the other buffer meanwhile
+      const int jn = blk(t + 1);
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0]);
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, jn * kBlkK, smem[buf ^ 1][1]);
     }
-    const uint16_t* Ks = smem[buf][0];
-    const uint16_t* Vs = smem[buf][1];
-
-    // ---- S^T = K Q^T : two 32-key slabs -------------------------------------------
-    f32x16 sc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      sc[0] = mfma32(lds_rowfrag<D>(Ks, 0, kk, lane), qf[kk], sc[0]);
-      sc[1] = mfma32(lds_rowfrag<D>(Ks, 32, kk, lane), qf[kk], sc[1]);
-    }
-    // keys at or beyond N exist only in the last key block
-    const int key0 = j * kBlkK;
-    if (key0 + kBlkK > N) {
-      const int lim = N - key0 - 8 * h;  // element e is valid iff acc_row(e,0) < lim
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = 16 * (e >> 3) + (e & 7);
-        if (r >= lim) sc[0][e] = -INFINITY;
-        if (r + 32 >= lim) sc[1][e] = -INFINITY;
-      }
-    }
-    // ---- online softmax (log2 domain, scale folded into the exponent) -------------------
-    float mloc = sc[0][0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sc[0][e]);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sc[1][e]);
-    mloc = fmaxf(mloc, swap_halves(mloc)) * scale_log2;
-    // With o_lo requested, P's rounding is carried by the lo half and the running maximum
-    // may lag the true one by up to 8 (log2 units).  Without it the maximum is exact, so the
-    // dominant probability of a peaked row is exactly 1 and rounds without error.
-    constexpr float kSlack = SPLIT ? 8.0f : 0.0f;
-    const bool raise = mloc > m_run + kSlack;
-    if (__ballot(raise)) {
-      const float m_new = raise ? mloc : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-    }
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sc[0][e] = __builtin_amdgcn_exp2f(fmaf(sc[0][e], scale_log2, -m_run));
-      sc[1][e] = __builtin_amdgcn_exp2f(fmaf(sc[1][e], scale_log2, -m_run));
-      psum += sc[0][e] + sc[1][e];
-    }
-    l_run += psum;
-    // ---- O^T += V^T P^T ---------------------------------------------------------------
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 ph, pl;
-      if constexpr (SPLIT)
-        split_bf16x8(sc[kk >> 1], kk & 1, ph, pl);
-      else
-        ph = to_bf16x8(sc[kk >> 1], kk & 1);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 va = lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
-        oacc[db] = mfma32(va, ph, oacc[db]);
-        if constexpr (SPLIT) oacc[db] = mfma32(va, pl, oacc[db]);
-      }
-    }
+    fwd_tile<D, SPLIT>(smem[buf][0], smem[buf][1], blk(t) * kBlkK, N, qf, oacc, m_run, l_run,
+                       scale_log2, lane);
     wait_vmem();
     __syncthreads();
   }

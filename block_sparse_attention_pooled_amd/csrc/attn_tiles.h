@@ -29,86 +29,81 @@ struct Tile {
   }
 };
 
-// Stage rows [row0, row0 + NROWS) of a [N, D] bf16 matrix into registers, NT threads.
-// Rows at or beyond N are read from row N-1 instead: their values are never used
-// (scores of such keys are masked, queries beyond N are not written).
-template <int D, int NROWS, int NT>
-struct Stager {
-  static constexpr int CHUNKS = NROWS * D / 8;
-  static constexpr int PER = CHUNKS / NT;
-  static_assert(CHUNKS % NT == 0, "tile chunks must divide among the threads");
-  uint4 r[PER];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int row0, int N) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int x = threadIdx.x + NT * u;
-      const int row = min(row0 + x / Tile<D>::CPR, N - 1);
-      r[u] = *reinterpret_cast<const uint4*>(base + (size_t)row * D + (x % Tile<D>::CPR) * 8);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds) const {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int x = threadIdx.x + NT * u;
-      *reinterpret_cast<uint4*>(lds + Tile<D>::off(x / Tile<D>::CPR, (x % Tile<D>::CPR) * 8)) = r[u];
-    }
-  }
-};
-
-// Direct global -> LDS staging (global_load_lds_dwordx4): each wave instruction writes
-// 64 lanes x 16 bytes to one contiguous 1 KB LDS segment (lane l at byte 16*l), so the
-// swizzle is applied on the global side: lane l of segment s fetches the chunk that
-// belongs at LDS chunk 64*s + l.  Rows at or beyond N are fetched from row N-1.
-// The caller waits (vmcnt) and synchronises before reading the tile.
-template <int D, int NROWS, int NWAVES>
-__device__ __forceinline__ void tile_load_lds(const uint16_t* __restrict__ base, int row0, int N,
-                                              uint16_t* lds) {
-  constexpr int SEGS = NROWS * D * 2 / 1024;   // 1 KB segments per tile
-  constexpr int PER = SEGS / NWAVES;
-  constexpr int RPS = 1024 / (D * 2);          // rows per segment
-  static_assert(SEGS % NWAVES == 0, "segments must divide among the waves");
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int seg = wv * PER + u;
-    const int row = seg * RPS + lane / Tile<D>::CPR;
-    const int pc = lane % Tile<D>::CPR;
-    const int cc = pc ^ Tile<D>::swz(row);
-    const int grow = min(row0 + row, N - 1);
-    __builtin_amdgcn_global_load_lds(base + (size_t)grow * D + cc * 8,
-                                     (SPA_LDS void*)(lds + seg * 512), 16, 0, 0);
-  }
+// Raw buffer resource over [base, base + bytes) in four scalar registers: loads beyond
+// the range return zeros.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu);  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = 0x00020000u;
+  return r;
 }
 
-// Raw buffer resource over [base, base + bytes): loads beyond the range return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+// One buffer->LDS transfer of 16 bytes per lane: lane l's bytes land at LDS byte address
+// lds_addr + 16*l.  Issued as inline assembly so that the compiler's wait-count tracking
+// does not see it: it would otherwise make every LDS read wait for all transfers still in
+// flight (it cannot tell which buffer they target), exposing the load latency each step.
+// The caller waits (wait_vmem) and synchronises before reading the data.  M0 is restored.
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t soff,
+                                      uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
+      : "memory");
 }
 
-// The same tile staging through a buffer resource over one head's [N, D] matrix: the
-// per-lane offsets are loop invariant (the tile's first row enters as a scalar offset), and
-// rows at or beyond N read as zeros (the range check of the resource) instead of being
-// clamped.
+// The same with 4 bytes per lane (lane l's word at lds_addr + 4*l).
+__device__ __forceinline__ void dma4(const u32x4& rsrc, uint32_t voff, uint32_t soff,
+                                     uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+// Tile staging through a buffer resource over one head's [N, D] matrix: the per-lane
+// offsets are loop invariant (the tile's first row enters as a scalar offset), and rows
+// at or beyond N read as zeros (the range check of the resource).
 template <int D, int NROWS, int NWAVES>
-__device__ __forceinline__ void tile_load_lds_rsrc(__amdgpu_buffer_rsrc_t rsrc, int row0,
-                                                   uint16_t* lds) {
+__device__ __forceinline__ void tile_load_lds_rsrc(const u32x4& rsrc, int row0, uint16_t* lds) {
   constexpr int SEGS = NROWS * D * 2 / 1024;
   constexpr int PER = SEGS / NWAVES;
   constexpr int RPS = 1024 / (D * 2);
   static_assert(SEGS % NWAVES == 0, "segments must divide among the waves");
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int seg = wv * PER + u;
     const int row = seg * RPS + lane / Tile<D>::CPR;
     const int cc = (lane % Tile<D>::CPR) ^ Tile<D>::swz(row);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (SPA_LDS void*)(lds + seg * 512), 16,
-                                             (row * D + cc * 8) * 2, row0 * D * 2, 0, 0);
+    dma16(rsrc, (uint32_t)(row * D + cc * 8) * 2, (uint32_t)row0 * D * 2,
+          lds_addr(lds + seg * 512));
   }
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone), issued through the builtin so that
+// the compiler's own wait-count bookkeeping knows every vector memory load has landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // A (or B) operand holding X[r0 + perm32(c)][16*kk + 8*h .. +7] for lane c + 32*h.
 template <int D>
