@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work to time for the baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, run a plain device copy of this size (the "
+                         "scale reference for memory-traffic counter passes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer shards by "
@@ -186,10 +189,20 @@ def main():
     dom = max(work, key=lambda n: stage_ms[n])
     bound, units_per_launch, unit, peak = work[dom]
     achieved = units_per_launch / (stage_ms[dom] * 1e-3)
+    from block_sparse_attention_pooled_amd import traffic as traffic_rec
     roofline = {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": None}
+                "frac": achieved / peak, "traffic": traffic_rec.load(dom, w.name)}
     attn_ms = stage_ms["fwd"] + stage_ms["bwd_prep"] + stage_ms["bwd_dkdv"] + stage_ms["bwd_dq"]
     mask_ms = stage_ms["mask_pool"] + stage_ms["mask_select"]
+
+    if args.calib_copy_mib > 0:  # scale reference for the traffic counters
+        n = args.calib_copy_mib << 20
+        src_buf = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        for _ in range(3):
+            dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
 
     # ---- dense-mask run on the same kernels ---------------------------------------------
     dense = None
