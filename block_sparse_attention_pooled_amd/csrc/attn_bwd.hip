@@ -161,11 +161,10 @@ __device__ __forceinline__ void dkdv_load_stage(const DkdvSrc& src, int qb, int 
 #define SPA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Producer, first half: S and P for the unit; P goes to LDS for the consumer.
-template <int D>
+template <int D, bool TAIL>
 __device__ __forceinline__ void dkdv_scores(const uint16_t* tq, const float* sd, float* pw,
                                             const bf16x8 (&kf)[D / 16], int r0, int lane,
-                                            bool tail, float kmask, float scale_log2,
-                                            f32x16& sacc) {
+                                            float kmask, float scale_log2, f32x16& sacc) {
   constexpr int KS = D / 16;
   const int h = lane >> 5;
   bf16x8 a[KS];
@@ -188,7 +187,7 @@ __device__ __forceinline__ void dkdv_scores(const uint16_t* tq, const float* sd,
     sacc[4 * g + 2] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + 2], scale_log2, -lv[g].z));
     sacc[4 * g + 3] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * g + 3], scale_log2, -lv[g].w));
   }
-  if (tail) {
+  if constexpr (TAIL) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) sacc[e] *= kmask;
   }
@@ -220,16 +219,18 @@ __device__ __forceinline__ void dkdv_dv(const uint16_t* tq, const f32x16& p, f32
   }
 }
 
-// Consumer, first half: dP for the unit.
 template <int D>
-__device__ __forceinline__ void dkdv_dp(const uint16_t* tq, const bf16x8 (&vf)[D / 16], int r0,
-                                        int lane, f32x16& dp) {
-  constexpr int KS = D / 16, HR = 64;
-  const uint16_t* dOb = tq + HR * D;
-  bf16x8 a[KS];
+__device__ __forceinline__ void dkdv_rowfrags(const uint16_t* tile, int r0, int lane,
+                                              bf16x8 (&a)[D / 16]) {
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) a[kk] = lds_rowfrag<D>(dOb, r0, kk, lane);
-  SPA_FENCE();
+  for (int kk = 0; kk < D / 16; ++kk) a[kk] = lds_rowfrag<D>(tile, r0, kk, lane);
+}
+
+// Consumer, first half: dP for the unit from dO row fragments read into registers.
+template <int D>
+__device__ __forceinline__ void dkdv_dp(const bf16x8 (&a)[D / 16], const bf16x8 (&vf)[D / 16],
+                                        f32x16& dp) {
+  constexpr int KS = D / 16;
   dp = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) dp = mfma32(a[kk], vf[kk], dp);
@@ -340,31 +341,41 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   // One step: loads of stage st+1 into the next slot, producer on stage st, consumer on
   // stage st-1.  Each job runs its own copy of the loop (same barriers), so that neither
   // keeps the other's loop-invariant addresses alive.
-#define SPA_DKDV_LOOP(JOB)                                                                   \
+#define SPA_DKDV_LOOP(...)                                                                   \
   {                                                                                        \
     int cur = 0, prev = 2;                                                                 \
     for (int st = 0; st <= nst; ++st) {                                                    \
       const int nxt = cur == 2 ? 0 : cur + 1;                                              \
       if (st + 1 < nst)                                                                    \
         dkdv_load_stage<D, BQ>(src, list_at(st + 1), st + 1, w, lane, tiles[nxt], side[nxt]); \
-      JOB;                                                                                 \
+      __VA_ARGS__;                                                                         \
       wait_vmem();                                                                         \
       __syncthreads();                                                                     \
       prev = cur;                                                                          \
       cur = nxt;                                                                           \
     }                                                                                      \
   }
-  if (role == 0) {
+  if (role == 0 && tail) {  // keys at or beyond N exist only in the last key block
     SPA_DKDV_LOOP(if (st < nst) {
       f32x16 p;
-      dkdv_scores<D>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane, tail,
-                     kmask, scale_log2, p);
+      dkdv_scores<D, true>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane,
+                           kmask, scale_log2, p);
+      dkdv_dv<D>(tiles[cur], p, acc, r0, lane);
+    })
+  } else if (role == 0) {
+    SPA_DKDV_LOOP(if (st < nst) {
+      f32x16 p;
+      dkdv_scores<D, false>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane,
+                            kmask, scale_log2, p);
       dkdv_dv<D>(tiles[cur], p, acc, r0, lane);
     })
   } else {
     SPA_DKDV_LOOP(if (st >= 1) {
+      bf16x8 a[KS];
+      dkdv_rowfrags<D>(tiles[prev] + HR * D, r0, lane, a);
+      SPA_FENCE();
       f32x16 dp;
-      dkdv_dp<D>(tiles[prev], bf, r0, lane, dp);
+      dkdv_dp<D>(a, bf, dp);
       dkdv_dk<D>(tiles[prev], side[prev], pbuf[(st - 1) & 1] + unit * 1024, dp, acc, r0, lane);
     })
   }
@@ -406,6 +417,60 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
 // dQ: one workgroup per query block (XCD-contiguous order), one wavefront per 32 rows;
 // K and V tiles staged like the forward pass.
 // ------------------------------------------------------------------------------------
+// One kept tile for this wave's 32 query rows: per 32-key slab S and dP (K, V fragments
+// read in batches of four k-steps), dS = P (dP - D), dQ += dS K with dS as a bf16 hi + lo
+// pair.  K and V rows at or beyond N were staged as zeros; TAIL masks their dS.
+template <int D, bool TAIL>
+__device__ __forceinline__ void dq_tile(const uint16_t* Ks, const uint16_t* Vs, int key0, int N,
+                                        const bf16x8 (&qf)[D / 16], const bf16x8 (&df)[D / 16],
+                                        float lse2, float dq_sum, f32x16 (&acc)[D / 32],
+                                        float scale_log2, int lane) {
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  const int h = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int k0 = 0; k0 < KS; k0 += 4) {
+      bf16x8 ka[4], va[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ka[u] = lds_rowfrag<D>(Ks, 32 * kb, k0 + u, lane);
+        va[u] = lds_rowfrag<D>(Vs, 32 * kb, k0 + u, lane);
+      }
+      SPA_FENCE();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s = mfma32(ka[u], qf[k0 + u], s);
+        dp = mfma32(va[u], df[k0 + u], dp);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -lse2));
+      dp[e] = pe * (dp[e] - dq_sum);
+    }
+    if constexpr (TAIL) {
+      const int lim = N - key0 - 32 * kb - 8 * h;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (16 * (e >> 3) + (e & 7) >= lim) dp[e] = 0.f;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 dh, dl;
+      split_bf16x8(dp, half, dh, dl);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 kt = lds_colfrag<D>(Ks, 32 * kb + 16 * half, 32 * db, lane);
+        acc[db] = mfma32(kt, dh, acc[db]);
+        acc[db] = mfma32(kt, dl, acc[db]);
+      }
+    }
+  }
+}
+
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -458,51 +523,26 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   }
   wait_vmem();  // also the row fragments: nothing vector-memory is pending inside the loop
   __syncthreads();
-  for (int t = 0; t < cnt; ++t) {
+  // only the last key block of the list can be partial: it gets its own instantiation of
+  // the tile body after the loop, so that the loop carries no per-element selects
+  const bool tail_last = cnt > 0 && blk(cnt - 1) * kBlkK + kBlkK > N;
+  const int cnt_main = cnt - (tail_last ? 1 : 0);
+  for (int t = 0; t < cnt_main; ++t) {
     const int buf = t & 1;
-    const int j = blk(t);
     if (t + 1 < cnt) {  // the next tile streams into the other buffer meanwhile
       const int jn = blk(t + 1);
       tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0]);
       tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, jn * kBlkK, smem[buf ^ 1][1]);
     }
-    const uint16_t* Ks = smem[buf][0];
-    const uint16_t* Vs = smem[buf][1];
-    const int key0 = j * kBlkK;
-    // one 32-key slab at a time: scores, dP, dS, then its two 16-key steps of dQ
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        s = mfma32(lds_rowfrag<D>(Ks, 32 * kb, kk, lane), qf[kk], s);
-        dp = mfma32(lds_rowfrag<D>(Vs, 32 * kb, kk, lane), df[kk], dp);
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -lse2));
-        dp[e] = pe * (dp[e] - dq_sum);
-      }
-      if (key0 + kBlkK > N) {  // keys at or beyond N exist only in the last key block
-        const int lim = N - key0 - 32 * kb - 8 * h;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (16 * (e >> 3) + (e & 7) >= lim) dp[e] = 0.f;
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 dh, dl;
-        split_bf16x8(dp, half, dh, dl);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 ka = lds_colfrag<D>(Ks, 32 * kb + 16 * half, 32 * db, lane);
-          acc[db] = mfma32(ka, dh, acc[db]);
-          acc[db] = mfma32(ka, dl, acc[db]);
-        }
-      }
-    }
+    dq_tile<D, false>(smem[buf][0], smem[buf][1], blk(t) * kBlkK, N, qf, df, lse2, dq_sum, acc,
+                      scale_log2, lane);
     wait_vmem();
     __syncthreads();
+  }
+  if (tail_last) {
+    const int buf = cnt_main & 1;
+    dq_tile<D, true>(smem[buf][0], smem[buf][1], blk(cnt_main) * kBlkK, N, qf, df, lse2, dq_sum,
+                     acc, scale_log2, lane);
   }
   if (qvalid) {
 #pragma unroll

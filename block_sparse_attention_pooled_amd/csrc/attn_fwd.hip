@@ -30,7 +30,7 @@ namespace spa {
 
 // One kept tile: S^T for this wave's 32 query rows, online softmax update, O^T += V^T P^T.
 // K and V rows at or beyond N were staged as zeros; their scores are masked here.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool TAIL>
 __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs, int key0, int N,
                                          const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
                                          float& m_run, float& l_run, float scale_log2, int lane) {
@@ -54,8 +54,9 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
       sc[1] = mfma32(a1[u], qf[k0 + u], sc[1]);
     }
   }
-  // keys at or beyond N exist only in the last key block
-  if (key0 + kBlkK > N) {
+  // keys at or beyond N exist only in the last key block (a separate instantiation, so
+  // that the other tiles carry no per-element selects)
+  if constexpr (TAIL) {
     const int lim = N - key0 - 8 * h;  // element e is valid iff acc_row(e,0) < lim
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -162,17 +163,26 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   }
   wait_vmem();  // also the Q fragments: nothing vector-memory is pending inside the loop
   __syncthreads();
-  for (int t = 0; t < cnt; ++t) {
+  // only the last key block of the list can be partial: it gets its own instantiation of
+  // the tile body after the loop, so that the loop carries no per-element selects
+  const bool tail_last = cnt > 0 && blk(cnt - 1) * kBlkK + kBlkK > N;
+  const int cnt_main = cnt - (tail_last ? 1 : 0);
+  for (int t = 0; t < cnt_main; ++t) {
     const int buf = t & 1;
     if (t + 1 < cnt) {  // the next tile streams into the other buffer meanwhile
       const int jn = blk(t + 1);
       tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0]);
       tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, jn * kBlkK, smem[buf ^ 1][1]);
     }
-    fwd_tile<D, SPLIT>(smem[buf][0], smem[buf][1], blk(t) * kBlkK, N, qf, oacc, m_run, l_run,
-                       scale_log2, lane);
+    fwd_tile<D, SPLIT, false>(smem[buf][0], smem[buf][1], blk(t) * kBlkK, N, qf, oacc, m_run,
+                              l_run, scale_log2, lane);
     wait_vmem();
     __syncthreads();
+  }
+  if (tail_last) {
+    const int buf = cnt_main & 1;
+    fwd_tile<D, SPLIT, true>(smem[buf][0], smem[buf][1], blk(cnt_main) * kBlkK, N, qf, oacc,
+                             m_run, l_run, scale_log2, lane);
   }
 
   // ---- epilogue ---------------------------------------------------------------------
