@@ -1,0 +1,114 @@
+"""GPU parity on the mask-rule stress layer at full size (B=1, H=12, N=32760, d=128, blocks
+128 x 64): heads 0-5 near-uniform (Q scaled by 0.1), heads 6-11 sink-dominated.
+
+For each (k, p) of the sweep k in {2, 5, 10} %, p in {0.7, 0.9, 0.95} the mask of two
+uniform and two sink heads is compared row by row with the oracle, including the rule
+lengths (Lk, Lp); the per-rule row counts are logged.  At k = 5 %, p = 0.9 the attention
+outputs and gradients are compared on sampled blocks of both head kinds.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_pooled_amd as spa
+from block_sparse_attention_pooled_amd import synth
+from oracle import spa_oracle as O
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS["stress"]
+SWEEP = [(k, p) for k in (0.02, 0.05, 0.10) for p in (0.7, 0.9, 0.95)]
+HEADS = [0, 5, 6, 11]  # two near-uniform, two sink-dominated
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def st():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    log(f"[stress] generating {W.name} {W.shape()}")
+    g = synth.generate(W)
+    dev = {n: torch.from_numpy(g[n].view(np.int16)).view(torch.bfloat16).cuda() for n in g}
+    return dict(torch=torch, g=g, dev=dev, f64={})
+
+
+def _head(st, name, h):
+    key = (name, h)
+    if key not in st["f64"]:
+        st["f64"][key] = O.widen_bf16(st["g"][name][:, h:h + 1])
+    return st["f64"][key]
+
+
+@pytest.mark.parametrize("k_frac,p", SWEEP)
+def test_stress_mask_sweep(st, k_frac, p):
+    dev = st["dev"]
+    kv_idx, kv_cnt, rl = spa.build_mask(dev["q"], dev["k"], W.blk_q, W.blk_k, k_frac, p,
+                                        rule_len=True)
+    idx, cnt, rl = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), rl.cpu().numpy()
+    lk, lp = rl[..., 0], rl[..., 1]
+    uni, snk = slice(0, W.H // 2), slice(W.H // 2, W.H)
+    log(f"[stress k={k_frac} p={p}] density uniform {cnt[:, uni].mean() / W.n_kblk:.3f} "
+        f"sink {cnt[:, snk].mean() / W.n_kblk:.3f}; Top-p-bound rows uniform "
+        f"{(lp[:, uni] > lk[:, uni]).mean():.3f} sink {(lp[:, snk] > lk[:, snk]).mean():.3f}")
+    for hh in HEADS:
+        mask = O.build_mask(_head(st, "q", hh), _head(st, "k", hh), W.blk_q, W.blk_k, k_frac, p)
+        n, exempt, fails = parity.compare_mask_rows(idx[:, hh:hh + 1], cnt[:, hh:hh + 1],
+                                                    mask["rows"], p)
+        assert n == W.n_qblk
+        assert not fails, (hh, fails[:5])
+        exempt_rows = {e[0][2] for e in exempt}
+        for i, r in enumerate(mask["rows"][(0, 0)]):
+            assert lk[0, hh, i] == r["Lk"]
+            if i not in exempt_rows:
+                assert lp[0, hh, i] == r["Lp"], (hh, i, lp[0, hh, i], r["Lp"])
+    # the failure regimes the hybrid rule repairs: on uniform heads Top-p keeps far more
+    # than Top-k; on sink heads Top-k keeps more than Top-p
+    assert np.median(lp[:, uni]) > np.median(lk[:, uni])
+    assert np.median(lp[:, snk]) <= np.median(lk[:, snk])
+
+
+def test_stress_attention_sampled(st):
+    torch, dev = st["torch"], st["dev"]
+    k_frac, p = 0.05, 0.9
+    kv_idx, kv_cnt = spa.build_mask(dev["q"], dev["k"], W.blk_q, W.blk_k, k_frac, p)
+    o, lse, o_lo = spa.sparse_attn_fwd(dev["q"], dev["k"], dev["v"], kv_idx, kv_cnt, W.blk_q,
+                                       W.blk_k, with_residual=True)
+    dq, dk, dv = spa.sparse_attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, kv_idx,
+                                     kv_cnt, W.blk_q, W.blk_k, o_lo=o_lo)
+    torch.cuda.synchronize()
+    idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    for hh, i in ((2, 77), (8, 200)):
+        log(f"[stress] fwd/dQ head {hh} q-block {i} ({cnt[0, hh, i]} kept blocks)")
+        lists = parity.lists_from_gpu(idx[:, hh:hh + 1], cnt[:, hh:hh + 1])
+        f = {n: _head(st, n, hh) for n in ("q", "k", "v", "do")}
+        ro, rl = O.sparse_attn_fwd(f["q"], f["k"], f["v"], lists, W.blk_q, W.blk_k,
+                                   heads=[(0, 0)], qblocks=[i])
+        rdq, _, _ = O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, W.blk_q, W.blk_k,
+                                      heads=[(0, 0)], qblocks=[i])
+        s, e = i * W.blk_q, min(W.N, (i + 1) * W.blk_q)
+        for name, got, want in (("O", o[0, hh, s:e].float().cpu().numpy(), ro[0, 0, s:e]),
+                                ("LSE", lse[0, hh, s:e].cpu().numpy(), rl[0, 0, s:e]),
+                                ("dQ", dq[0, hh, s:e].cpu().numpy(), rdq[0, 0, s:e])):
+            ok, mx, rel, _ = parity.close(got, want)
+            log(f"  {name}: max_abs={mx:.3e} rel_l2={rel:.3e}")
+            assert ok, (name, mx, rel)
+    for hh, j in ((9, 0), (3, 311)):
+        lists = parity.lists_from_gpu(idx[:, hh:hh + 1], cnt[:, hh:hh + 1])
+        users = [i for i, keep in enumerate(lists[(0, 0)]) if j in set(keep.tolist())]
+        log(f"[stress] dK/dV head {hh} key block {j}, kept by {len(users)} query blocks")
+        f = {n: _head(st, n, hh) for n in ("q", "k", "v", "do")}
+        _, rdk, rdv = O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, W.blk_q,
+                                        W.blk_k, heads=[(0, 0)], qblocks=users)
+        s, e = j * W.blk_k, min(W.N, (j + 1) * W.blk_k)
+        for name, got, want in (("dK", dk[0, hh, s:e].cpu().numpy(), rdk[0, 0, s:e]),
+                                ("dV", dv[0, hh, s:e].cpu().numpy(), rdv[0, 0, s:e])):
+            ok, mx, rel, _ = parity.close(got, want)
+            log(f"  {name}: max_abs={mx:.3e} rel_l2={rel:.3e}")
+            assert ok, (name, mx, rel)
