@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work to time for the baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="extra steps timed with the 256 MB last-level cache flushed before "
+                         "each (a secondary, cold-cache figure)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this size (the "
                          "scale reference for memory-traffic counter passes)")
@@ -195,6 +198,38 @@ def main():
     attn_ms = stage_ms["fwd"] + stage_ms["bwd_prep"] + stage_ms["bwd_dkdv"] + stage_ms["bwd_dq"]
     mask_ms = stage_ms["mask_pool"] + stage_ms["mask_select"]
 
+    # ---- cold-cache steps: reading 512 MB evicts the 256 MB last-level cache before each
+    # step (a read, so that no dirty lines are written back during the step) -------------
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)]
+               for _ in range(args.cold_steps)]
+        for s_ in range(args.cold_steps):
+            float(flush.sum())
+            torch.cuda.synchronize()
+            step(cev[s_])
+            torch.cuda.synchronize()
+        cold_stage = {name: float(np.mean([cev[s_][i].elapsed_time(cev[s_][i + 1])
+                                           for s_ in range(args.cold_steps)]))
+                      for i, name in enumerate(stage_names)}
+        cold = {"ms_per_step": float(np.mean([cev[s_][0].elapsed_time(cev[s_][6])
+                                              for s_ in range(args.cold_steps)])),
+                "stage_ms": cold_stage,
+                "mask_hbm_frac": mask_bytes / ((cold_stage["mask_pool"] + cold_stage["mask_select"])
+                                               * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del flush
+        log(f"[bench] cold-cache step {cold['ms_per_step']:.3f} ms")
+
+    # ---- rule statistics of the measured mask -------------------------------------------
+    _, _, rl = spa.build_mask(q, k, w.blk_q, w.blk_k, w.k_frac, w.p, rule_len=True)
+    rl_h = rl.cpu().numpy()
+    lk_h, lp_h = rl_h[..., 0], rl_h[..., 1]
+    rules = {"Lk": int(lk_h.flat[0]), "mean_Lp": float(lp_h.mean()),
+             "mean_L": float(cnt_h.mean()), "rows_topp_bound": float((lp_h > lk_h).mean()),
+             "L_percentiles_50_90_99_100": [float(x) for x in
+                                            np.percentile(cnt_h, [50, 90, 99, 100])]}
+
     if args.calib_copy_mib > 0:  # scale reference for the traffic counters
         n = args.calib_copy_mib << 20
         src_buf = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -242,6 +277,7 @@ def main():
         "credited_tflops_fwd_bwd": fl_total / (attn_ms * 1e-3) / 1e12,
         "mfma_util_credited": fl_total / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "mask_hbm_frac": mask_bytes / (mask_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "rules": rules, "cold_cache": cold,
         "roofline": roofline, "dense": dense, "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -41,10 +41,19 @@ __global__ __launch_bounds__(256) void k_pool(const uint16_t* __restrict__ q,
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-#pragma unroll 4
-  for (int rr = r; rr < nrows; rr += R) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)rr * D + c * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // all of this thread's loads of a 128-row block are issued before the first one is
+  // used (rows at or beyond N are read as zeros and not counted)
+  constexpr int PASSES = 128 / R;
+  uint4 v[PASSES];
+#pragma unroll
+  for (int u = 0; u < PASSES; ++u) {
+    const int rr = r + u * R;
+    v[u] = rr < nrows ? *reinterpret_cast<const uint4*>(src + (size_t)rr * D + c * 8)
+                      : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < PASSES; ++u) {
+    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc[2 * e] += (double)bf16_bits_to_f32(w[e] & 0xFFFFu);

@@ -6,6 +6,8 @@ calibrated against a plain device-to-device copy of known size recorded in the s
 the kernel sources it was measured with: once those sources change, the figure is stale
 and ``load`` returns None.
 
+Also summarises an executed-MFMA counter pass (``summarize-mfma``).
+
 Command line (writes the markdown summary to stdout):
 
     python -m block_sparse_attention_pooled_amd.traffic summarize \
@@ -117,6 +119,41 @@ def load(stage: str, workload: str):
     return None
 
 
+def summarize_mfma(csv_path, workload, command) -> str:
+    """Executed MFMA work per dispatch from SQ_INSTS_MFMA (every MFMA here is a
+    32x32x16 bf16 instruction: 32768 FLOP per wavefront instruction) over the dispatch's
+    duration, with the MFMA-busy and GPU-busy cycle counters as recorded."""
+    per = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(dict)
+    with open(csv_path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+            per[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[name][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = [f"# Executed MFMA work per launch: {workload}", "",
+           "Counter pass (from the repository root on one MI355X):", "", "```", command, "```",
+           "",
+           "Executed FLOP = SQ_INSTS_MFMA x 32768 (all MFMAs are v_mfma_f32_32x32x16_bf16); "
+           "the rate divides by the dispatch's own duration in this run.  Credited (kept-tile "
+           "algorithmic) FLOP are lower: the precision splits and the recomputation in the "
+           "backward are executed but not credited.", "",
+           "| kernel | dispatches | MFMA instr / dispatch | executed TFLOP / dispatch | "
+           "duration us | executed TFLOP/s | SQ_VALU_MFMA_BUSY_CYCLES | SQ_BUSY_CYCLES | "
+           "GRBM_GUI_ACTIVE |", "|---|---|---|---|---|---|---|---|---|"]
+    for name in sorted(per, key=lambda n: -sum(dur[n].values())):
+        c = per[name]
+        mf = c.get("SQ_INSTS_MFMA")
+        if not mf or max(mf) == 0:
+            continue
+        avg = lambda k: sum(c[k]) / len(c[k]) if c.get(k) else float("nan")
+        d_us = sum(dur[name].values()) / len(dur[name]) / 1e3
+        tf = avg("SQ_INSTS_MFMA") * 32768 / 1e12
+        out.append(f"| `{name}` | {len(dur[name])} | {avg('SQ_INSTS_MFMA'):.4g} | {tf:.4f} | "
+                   f"{d_us:.1f} | {tf / (d_us * 1e-6):.0f} | {avg('SQ_VALU_MFMA_BUSY_CYCLES'):.4g} | "
+                   f"{avg('SQ_BUSY_CYCLES'):.4g} | {avg('GRBM_GUI_ACTIVE'):.4g} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="block_sparse_attention_pooled_amd.traffic")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -127,9 +164,16 @@ def main(argv=None):
     s.add_argument("--workload", required=True)
     s.add_argument("--command-fetch", required=True)
     s.add_argument("--command-write", required=True)
+    m = sub.add_parser("summarize-mfma")
+    m.add_argument("--csv", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    sys.stdout.write(summarize(a.fetch, a.write, a.copy_mib, a.workload, a.command_fetch,
-                               a.command_write))
+    if a.cmd == "summarize":
+        sys.stdout.write(summarize(a.fetch, a.write, a.copy_mib, a.workload, a.command_fetch,
+                                   a.command_write))
+    else:
+        sys.stdout.write(summarize_mfma(a.csv, a.workload, a.command))
 
 
 if __name__ == "__main__":
