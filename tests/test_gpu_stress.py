@@ -4,7 +4,8 @@
 For each (k, p) of the sweep k in {2, 5, 10} %, p in {0.7, 0.9, 0.95} the mask of two
 uniform and two sink heads is compared row by row with the oracle, including the rule
 lengths (Lk, Lp); the per-rule row counts are logged.  At k = 5 %, p = 0.9 the attention
-outputs and gradients are compared on sampled blocks of both head kinds.
+outputs and gradients are compared on sampled blocks of both head kinds, and the kept
+attention mass of Top-k alone, Top-p alone and the union is checked row by row.
 """
 import sys
 
@@ -112,3 +113,29 @@ def test_stress_attention_sampled(st):
             ok, mx, rel, _ = parity.close(got, want)
             log(f"  {name}: max_abs={mx:.3e} rel_l2={rel:.3e}")
             assert ok, (name, mx, rel)
+
+
+def test_rule_superset_kept_mass(st):
+    """The union keeps a superset of either rule's blocks, so its kept attention mass
+    exp(LSE_rule - LSE_dense) is at least either rule's, row by row (the ablation's
+    comparison, as an invariant)."""
+    torch, dev = st["torch"], st["dev"]
+
+    def lse_of(k_frac, p):
+        kv_idx, kv_cnt = spa.build_mask(dev["q"], dev["k"], W.blk_q, W.blk_k, k_frac, p)
+        _, lse = spa.sparse_attn_fwd(dev["q"], dev["k"], dev["v"], kv_idx, kv_cnt, W.blk_q,
+                                     W.blk_k)
+        return lse.double()
+
+    dense = lse_of(1.0, 1.0)
+    mass = {r: torch.exp(lse_of(kf, p) - dense) for r, (kf, p) in
+            {"k": (0.05, 0.0), "p": (0.0, 0.9), "union": (0.05, 0.9)}.items()}
+    tol = 1e-5
+    assert bool((mass["union"] >= mass["k"] - tol).all())
+    assert bool((mass["union"] >= mass["p"] - tol).all())
+    assert bool((mass["union"] <= 1.0 + tol).all())
+    uni, snk = slice(0, W.H // 2), slice(W.H // 2, W.H)
+    # uniform heads: the fixed count alone keeps little mass; sink heads: the mass target
+    # alone can stop at the sink block and lose most of a row's mass
+    assert float(mass["k"][:, uni].mean()) < 0.5 < float(mass["union"][:, uni].mean())
+    assert float(mass["p"][:, snk].min()) < float(mass["union"][:, snk].min())
