@@ -7,8 +7,10 @@ sparse forward with the residual output the backward needs, and saves the kept-b
 so that the backward pass uses the same mask (the mask is held fixed: no gradient flows
 through the selection).  ``SpargeAttention`` is the ``nn.Module`` around it.
 
-Tensors are [B, H, N, d] bf16 on a ROCm device; gradients come back in the input dtype
-(bf16).  Every step runs in the library's kernels; this file only marshals arguments.
+Tensors are [B, H, N, d] on a ROCm device.  The kernels compute in bf16: other input
+dtypes (fp32 master activations, fp16) are rounded to bf16 on the way in, and the output and
+the gradients come back in the input dtype.  Every step runs in the library's kernels; this
+file only marshals arguments.
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ class SparseAttentionFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, k_frac: float, p: float, blk_q: int, blk_k: int, scale,
                 pooled_scale, mask=None):
-        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        ctx.in_dtype = q.dtype
+        q, k, v = (t.to(torch.bfloat16).contiguous() for t in (q, k, v))
         if mask is None:
             kv_idx, kv_cnt = build_mask(q, k, blk_q, blk_k, k_frac, p,
                                         pooled_scale=pooled_scale)
@@ -31,7 +34,7 @@ class SparseAttentionFunction(torch.autograd.Function):
                                        with_residual=True)
         ctx.save_for_backward(q, k, v, o, o_lo, lse, kv_idx, kv_cnt)
         ctx.cfg = (blk_q, blk_k, scale)
-        return o
+        return o.to(ctx.in_dtype)
 
     @staticmethod
     def backward(ctx, do):
@@ -40,6 +43,7 @@ class SparseAttentionFunction(torch.autograd.Function):
         dq, dk, dv = sparse_attn_bwd(q, k, v, o, do.contiguous().to(torch.bfloat16), lse,
                                      kv_idx, kv_cnt, blk_q, blk_k, scale, o_lo=o_lo,
                                      grad_dtype=torch.bfloat16)
+        dq, dk, dv = (g.to(ctx.in_dtype) for g in (dq, dk, dv))
         return dq, dk, dv, None, None, None, None, None, None, None
 
 
@@ -53,7 +57,10 @@ def sparse_attention(q, k, v, k_frac: float = 0.05, p: float = 0.9, blk_q: int =
 
 
 class SpargeAttention(torch.nn.Module):
-    """Drop-in attention layer: ``forward(q, k, v)`` with [B, H, N, d] bf16 tensors."""
+    """Drop-in attention layer: ``forward(q, k, v)`` with [B, H, N, d] tensors.
+
+    With ``keep_mask = True`` the kept-block lists of the last call stay in ``last_mask``
+    (for inspection, or to rerun the same mask elsewhere)."""
 
     def __init__(self, k_frac: float = 0.05, p: float = 0.9, blk_q: int = 128,
                  blk_k: int = 64, scale: float | None = None,
@@ -62,8 +69,16 @@ class SpargeAttention(torch.nn.Module):
         self.k_frac, self.p = float(k_frac), float(p)
         self.blk_q, self.blk_k = int(blk_q), int(blk_k)
         self.scale, self.pooled_scale = scale, pooled_scale
+        self.keep_mask = False
+        self.last_mask = None
 
     def forward(self, q, k, v, mask=None):
+        if mask is None and self.keep_mask:
+            mask = build_mask(q.detach().to(torch.bfloat16).contiguous(),
+                              k.detach().to(torch.bfloat16).contiguous(), self.blk_q,
+                              self.blk_k, self.k_frac, self.p, pooled_scale=self.pooled_scale)
+        if self.keep_mask:
+            self.last_mask = mask
         return sparse_attention(q, k, v, self.k_frac, self.p, self.blk_q, self.blk_k,
                                 self.scale, self.pooled_scale, mask)
 
