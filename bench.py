@@ -136,7 +136,7 @@ def main():
     bws = torch.empty(spa.bwd_workspace_bytes(q.shape, w.blk_q, w.blk_k), dtype=torch.uint8,
                       device=dev)
     stream = torch.cuda.current_stream(dev)
-    stage_names = ["mask_pool", "mask_select", "fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
+    stage_names = ["mask_pool", "mask_select", "fwd", "bwd_prep", "bwd_dq", "bwd_dkdv"]
 
     def step(events=None, k_frac=w.k_frac, p=w.p):
         def mark(idx):
@@ -152,7 +152,7 @@ def main():
         spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k, with_residual=True,
                             out=(o, lse, o_lo))
         mark(3)
-        for st, idx in ((spa.BWD_PREP, 4), (spa.BWD_DKDV, 5), (spa.BWD_DQ, 6)):
+        for st, idx in ((spa.BWD_PREP, 4), (spa.BWD_DQ, 5), (spa.BWD_DKDV, 6)):
             spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k, o_lo=o_lo,
                                 out=(dq, dk, dv), workspace=bws, stages=st)
             mark(idx)

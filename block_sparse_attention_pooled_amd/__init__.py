@@ -31,7 +31,7 @@ SYMBOLS = ("spa_mask_workspace_bytes", "spa_build_mask", "spa_build_mask_stages"
            "spa_sparse_attn_fwd", "spa_bwd_workspace_bytes", "spa_sparse_attn_bwd",
            "spa_sparse_attn_bwd_stages", "spa_status_string", "spa_version")
 MASK_POOL, MASK_SELECT, MASK_ALL = 1, 2, 3
-BWD_PREP, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
+BWD_PREP, BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 4, 7
 
 
 class SpaError(RuntimeError):

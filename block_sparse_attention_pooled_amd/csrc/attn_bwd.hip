@@ -4,15 +4,17 @@
 // Kernel-Implementierung und Modellanpassung").
 //
 // Launch sequence (one stream):
-//   k_dsum      D_t = <dO_t, O_t> in fp32, with O = o + o_lo when the forward pass
-//               supplied its rounding residual;
 //   k_bitmap    the kept-tile bitmap, transposed: word w of query block i at [w][i];
 //   k_collists  per key block j, the ascending list of query blocks that keep j;
+//   k_dq        one workgroup per (b, h, query block): first D_t = <dO_t, O_t> in fp32
+//               (O = o + o_lo when the forward pass supplied its rounding residual) and
+//               lse_t * log2(e) for its rows, kept in registers and written out for the
+//               next kernel; then walks its key-block list in ascending order and
+//               accumulates dQ += dS K;
 //   k_dkdv      one workgroup per (b, h, key block): walks its query-block list in
-//               ascending order, recomputes S and P, accumulates dV += P^T dO and
-//               dK += dS^T Q in registers (no atomics, fixed order);
-//   k_dq        one workgroup per (b, h, query block): walks its key-block list in
-//               ascending order and accumulates dQ += dS K.
+//               ascending order, recomputes S and P (reading D and lse * log2(e) that k_dq
+//               wrote), accumulates dV += P^T dO and dK += dS^T Q in registers (no atomics,
+//               fixed order).
 // All products are bf16 MFMA with fp32 accumulation.  P (in dV = P^T dO) and dS (in
 // dQ = dS K and dK = dS^T Q) enter as bf16 hi + lo pairs (about 16 bits): on peaked
 // rows dS is a difference of nearly equal terms, and dV of a key that many queries
@@ -22,55 +24,6 @@
 #include "spa_internal.h"
 
 namespace spa {
-
-// ------------------------------------------------------------------------------------
-// Per-row side values, padded to whole query blocks: D = rowsum(dO * O) and
-// lse2 = lse * log2(e).  Rows at or beyond N (padding) get D = 0 and lse2 = +inf, so that
-// their probabilities evaluate to exactly 0 wherever a staged tile holds such a row.
-// ------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void k_dsum(const uint16_t* __restrict__ o,
-                                              const uint16_t* __restrict__ o_lo,
-                                              const uint16_t* __restrict__ dout,
-                                              const float* __restrict__ lse, int N, int npad,
-                                              long long rows, float* __restrict__ dsum,
-                                              float* __restrict__ lse2) {
-  constexpr int CPR = D / 8;         // lanes per row
-  constexpr int RPB = 256 / CPR;     // rows per block
-  const long long prow = (long long)blockIdx.x * RPB + threadIdx.x / CPR;  // padded index
-  const int cc = threadIdx.x % CPR;
-  const long long bh = prow / npad;
-  const int r = (int)(prow - bh * npad);
-  const bool real = prow < rows && r < N;
-  const long long row = bh * N + r;  // unpadded index, valid when real
-  float acc = 0.f;
-  if (real) {
-    const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + cc * 8);
-    const uint4 b = *reinterpret_cast<const uint4*>(dout + row * D + cc * 8);
-    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
-    uint32_t wl[4] = {0u, 0u, 0u, 0u};
-    if (o_lo) {
-      const uint4 c = *reinterpret_cast<const uint4*>(o_lo + row * D + cc * 8);
-      wl[0] = c.x;
-      wl[1] = c.y;
-      wl[2] = c.z;
-      wl[3] = c.w;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float o0 = bf16_bits_to_f32(wa[e] & 0xFFFFu) + bf16_bits_to_f32(wl[e] & 0xFFFFu);
-      const float o1 = bf16_bits_to_f32(wa[e] >> 16) + bf16_bits_to_f32(wl[e] >> 16);
-      acc = fmaf(o0, bf16_bits_to_f32(wb[e] & 0xFFFFu), acc);
-      acc = fmaf(o1, bf16_bits_to_f32(wb[e] >> 16), acc);
-    }
-  }
-#pragma unroll
-  for (int off = CPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (prow < rows && cc == 0) {
-    dsum[prow] = acc;
-    lse2[prow] = real ? lse[row] * kLog2e : INFINITY;
-  }
-}
 
 // ------------------------------------------------------------------------------------
 // column lists
@@ -471,11 +424,38 @@ __device__ __forceinline__ void dq_tile(const uint16_t* Ks, const uint16_t* Vs, 
   }
 }
 
+// Per-row side values, for the padded rows of whole query blocks: D = rowsum(dO * O) and
+// lse2 = lse * log2(e).  Rows at or beyond N (padding) get D = 0 and lse2 = +inf, so that
+// their probabilities evaluate to exactly 0 wherever a staged tile holds such a row.
+template <int D>
+__device__ __forceinline__ float row_dsum(const uint16_t* o, const uint16_t* o_lo,
+                                          const bf16x8 (&df)[D / 16], size_t qoff) {
+  float acc = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + qoff + 16 * kk);
+    uint4 l = make_uint4(0u, 0u, 0u, 0u);
+    if (o_lo) l = *reinterpret_cast<const uint4*>(o_lo + qoff + 16 * kk);
+    const uint4 g = __builtin_bit_cast(uint4, df[kk]);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wl[4] = {l.x, l.y, l.z, l.w};
+    const uint32_t wg[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float o0 = bf16_bits_to_f32(wa[e] & 0xFFFFu) + bf16_bits_to_f32(wl[e] & 0xFFFFu);
+      const float o1 = bf16_bits_to_f32(wa[e] >> 16) + bf16_bits_to_f32(wl[e] >> 16);
+      acc = fmaf(o0, bf16_bits_to_f32(wg[e] & 0xFFFFu), acc);
+      acc = fmaf(o1, bf16_bits_to_f32(wg[e] >> 16), acc);
+    }
+  }
+  return acc + swap_halves(acc);  // the two lanes of a row hold its two column halves
+}
+
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse2p, const float* __restrict__ dsum,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ o_lo, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, float* __restrict__ lse2p, float* __restrict__ dsum,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int N, int npad,
     int nqb, int nkb, int total, float scale_log2, float scale, void* __restrict__ dq_out,
     int grad_bf16) {
@@ -507,9 +487,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     qf[kk] = *reinterpret_cast<const bf16x8*>(q + qoff + 16 * kk);
     df[kk] = *reinterpret_cast<const bf16x8*>(dout + qoff + 16 * kk);
   }
-  const size_t ri = (size_t)bh * npad + qrow;  // padded side arrays: rows beyond N hold P = 0
-  const float lse2 = lse2p[ri];
-  const float dq_sum = dsum[ri];
+  const float lse2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : INFINITY;
+  const float dq_sum = qvalid ? row_dsum<D>(o, o_lo, df, qoff) : 0.f;
+  if (h == 0) {  // padded side arrays for k_dkdv
+    const size_t ri = (size_t)bh * npad + qrow;
+    lse2p[ri] = lse2;
+    dsum[ri] = dq_sum;
+  }
 
   f32x16 acc[DB];
 #pragma unroll
@@ -599,10 +583,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
   const float sl2 = a.scale * kLog2e;
   const int npad = (int)n_pad(g);
   if (stages & 1u) {
-    const long long rows = (long long)g.bh() * npad;
-    constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((k_dsum<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s,
-                       a.o, a.o_lo, a.dout, a.lse, g.N, npad, rows, a.dsum, a.lse2);
     const int nw = n_words(g);
     hipLaunchKernelGGL(k_bitmap, dim3(g.nqb, (unsigned)g.bh()), dim3(64), 0, s, a.kv_idx,
                        a.kv_cnt, g.nqb, g.nkb, nw, a.bits);
@@ -610,16 +590,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
                        g.nqb * sizeof(uint32_t), s, a.bits, g.nqb, g.nkb, nw, a.q_idx, a.q_cnt);
   }
   if (stages & 2u) {
+    const int total = (int)(g.nqb * g.bh());
+    hipLaunchKernelGGL((k_dq<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.o,
+                       a.o_lo, a.dout, a.lse, a.lse2, a.dsum, a.kv_idx, a.kv_cnt, g.N, npad,
+                       g.nqb, g.nkb, total, sl2, a.scale, a.dq, a.grad_bf16);
+  }
+  if (stages & 4u) {
     const int total = (int)(g.nkb * g.bh());
     hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(total), dim3(512), 0, s, a.q, a.k, a.v, a.dout,
                        a.lse2, a.dsum, a.q_idx, a.q_cnt, g.N, npad, g.nqb, g.nkb, total, sl2,
                        a.scale, a.dk, a.dv, a.grad_bf16);
-  }
-  if (stages & 4u) {
-    const int total = (int)(g.nqb * g.bh());
-    hipLaunchKernelGGL((k_dq<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.dout,
-                       a.lse2, a.dsum, a.kv_idx, a.kv_cnt, g.N, npad, g.nqb, g.nkb, total, sl2,
-                       a.scale, a.dq, a.grad_bf16);
   }
   return hipGetLastError();
 }

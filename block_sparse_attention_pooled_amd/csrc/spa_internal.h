@@ -66,8 +66,8 @@ struct BwdArgs {
   void* dv;
   int grad_bf16;
   // workspace sections
-  float* dsum;      // [BH][nqb * blk_q]: D = rowsum(dO * O), 0 on padding rows
-  float* lse2;      // [BH][nqb * blk_q]: lse * log2(e), +inf on padding rows
+  float* dsum;      // [BH][nqb * blk_q]: D = rowsum(dO * O), 0 on padding rows (k_dq writes)
+  float* lse2;      // [BH][nqb * blk_q]: lse * log2(e), +inf on padding rows (k_dq writes)
   uint32_t* bits;   // [BH][ceil(nkb/32)][nqb]
   int32_t* q_idx;   // [BH][nkb][nqb]
   int32_t* q_cnt;   // [BH][nkb]

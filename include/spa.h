@@ -159,13 +159,14 @@ SPA_API int spa_sparse_attn_bwd(const spa_dims* dims, const void* q, const void*
  * in one call or several with the same arguments and workspace, equals the unstaged
  * call).  Stage bits of spa_build_mask_stages: SPA_MASK_POOL (block means of Q and K
  * into the workspace), SPA_MASK_SELECT (pooled softmax and selection from the
- * workspace).  Stage bits of spa_sparse_attn_bwd_stages: SPA_BWD_PREP (D and the
- * per-key-block query-block lists into the workspace), SPA_BWD_DKDV (dK, dV),
- * SPA_BWD_DQ (dQ).  A zero or unknown stage mask gives SPA_E_PARAM.
+ * workspace).  Stage bits of spa_sparse_attn_bwd_stages: SPA_BWD_PREP (the
+ * per-key-block query-block lists into the workspace), SPA_BWD_DQ (dQ; also writes D and
+ * lse * log2(e) of every row into the workspace), SPA_BWD_DKDV (dK, dV; reads what
+ * SPA_BWD_DQ wrote).  A zero or unknown stage mask gives SPA_E_PARAM.
  */
 enum {
   SPA_MASK_POOL = 1, SPA_MASK_SELECT = 2, SPA_MASK_ALL = 3,
-  SPA_BWD_PREP = 1, SPA_BWD_DKDV = 2, SPA_BWD_DQ = 4, SPA_BWD_ALL = 7
+  SPA_BWD_PREP = 1, SPA_BWD_DQ = 2, SPA_BWD_DKDV = 4, SPA_BWD_ALL = 7
 };
 
 SPA_API int spa_build_mask_stages(const spa_dims* dims, const void* q, const void* k,
