@@ -474,7 +474,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   const u32x4 krs = make_rsrc(k + head, (uint32_t)N * D * 2);
   const u32x4 vrs = make_rsrc(v + head, (uint32_t)N * D * 2);
   const int32_t* list = kv_idx + ((size_t)bh * nqb + i) * nkb;
-  const int cnt = kv_cnt[(size_t)bh * nqb + i];
+  // the lists are trusted; the clamp only keeps a corrupt count inside the LDS list
+  const int cnt = min(max(kv_cnt[(size_t)bh * nqb + i], 0), nkb);
   for (int x = threadIdx.x; x < cnt; x += NT) lst[x] = list[x];
   auto blk = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[min(t, cnt - 1)]); };
 

@@ -8,9 +8,9 @@ so that the backward pass uses the same mask (the mask is held fixed: no gradien
 through the selection).  ``SpargeAttention`` is the ``nn.Module`` around it.
 
 Tensors are [B, H, N, d] on a ROCm device.  The kernels compute in bf16: other input
-dtypes (fp32 master activations, fp16) are rounded to bf16 on the way in, and the output and
-the gradients come back in the input dtype.  Every step runs in the library's kernels; this
-file only marshals arguments.
+dtypes (fp32 master activations, fp16) are rounded to bf16 on the way in; the output comes
+back in q's dtype and each gradient in its input's dtype.  Every step runs in the library's
+kernels; this file only marshals arguments.
 """
 from __future__ import annotations
 
@@ -23,7 +23,8 @@ class SparseAttentionFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, k_frac: float, p: float, blk_q: int, blk_k: int, scale,
                 pooled_scale, mask=None):
-        ctx.in_dtype = q.dtype
+        ctx.in_dtypes = (q.dtype, k.dtype, v.dtype)
+        ctx.out_dtype = q.dtype
         q, k, v = (t.to(torch.bfloat16).contiguous() for t in (q, k, v))
         if mask is None:
             kv_idx, kv_cnt = build_mask(q, k, blk_q, blk_k, k_frac, p,
@@ -34,7 +35,7 @@ class SparseAttentionFunction(torch.autograd.Function):
                                        with_residual=True)
         ctx.save_for_backward(q, k, v, o, o_lo, lse, kv_idx, kv_cnt)
         ctx.cfg = (blk_q, blk_k, scale)
-        return o.to(ctx.in_dtype)
+        return o.to(ctx.out_dtype)
 
     @staticmethod
     def backward(ctx, do):
@@ -43,7 +44,7 @@ class SparseAttentionFunction(torch.autograd.Function):
         dq, dk, dv = sparse_attn_bwd(q, k, v, o, do.contiguous().to(torch.bfloat16), lse,
                                      kv_idx, kv_cnt, blk_q, blk_k, scale, o_lo=o_lo,
                                      grad_dtype=torch.bfloat16)
-        dq, dk, dv = (g.to(ctx.in_dtype) for g in (dq, dk, dv))
+        dq, dk, dv = (g.to(dt) for g, dt in zip((dq, dk, dv), ctx.in_dtypes))
         return dq, dk, dv, None, None, None, None, None, None, None
 
 
