@@ -5,9 +5,10 @@
   every row of both heads; O, LSE, dQ on the first, a middle and the last query block;
   dK, dV on the first, a middle and the last key block.
 - Near-maximal kept lists: unstructured inputs at N = 131035 (last key block 27 keys), where
-  the hybrid rule keeps about 1840 of 2048 blocks per row.  The mask is compared on every
-  row of one head, O, LSE, dQ on the last query block; dK and dV (whose oracle would need
-  nearly the dense layer) through invariants that hold at any size.
+  the hybrid rule keeps about 1840 of 2048 blocks per row; with 64-row query blocks the
+  per-key-block lists of the dK/dV pass near their 2048-entry capacity too.  The mask is
+  compared on every row of one head, O, LSE, dQ on the last query block; dK and dV (whose
+  oracle would need nearly the dense layer) through invariants that hold at any size.
 - bf16 gradients: the backward with ``grad_dtype=bfloat16`` must return exactly the
   round-to-nearest-even bf16 values of its fp32 gradients (same kernels, same arithmetic,
   one rounding at the store).
@@ -98,12 +99,22 @@ def test_max_length_sampled(torch_gpu, tag, w):
                 assert ok, (hh, j, name, mx, rel)
 
 
-def test_near_maximal_lists(torch_gpu):
+DENSE_CASES = [
+    # query blocks of 128 rows: row lists near 2048 entries
+    ("q128", synth.Workload("max_dense", 1, 2, 131072 - 37, 64, 128, 64, 0.05, 0.9,
+                            kind="tiny", seed=12)),
+    # query blocks of 64 rows: 2048 of them, so the per-key-block lists of the dK/dV pass
+    # also approach their 2048-entry capacity
+    ("q64", synth.Workload("max_dense_q64", 1, 1, 131072 - 37, 64, 64, 64, 0.05, 0.9,
+                           kind="tiny", seed=13)),
+]
+
+
+@pytest.mark.parametrize("tag,w", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_near_maximal_lists(torch_gpu, tag, w):
     torch = torch_gpu
-    w = synth.Workload("max_dense", 1, 2, 131072 - 37, 64, 128, 64, 0.05, 0.9, kind="tiny",
-                       seed=12)
     assert w.n_kblk == 2048 and w.N % 64 == 27
-    log(f"[limits dense lists] shape={w.shape()}")
+    log(f"[limits dense lists {tag}] shape={w.shape()} query blocks={w.n_qblk}")
     g = synth.generate(w)
     dev = {n: torch.from_numpy(g[n].view(np.int16)).view(torch.bfloat16).cuda() for n in g}
     kv_idx, kv_cnt = spa.build_mask(dev["q"], dev["k"], w.blk_q, w.blk_k, w.k_frac, w.p)
@@ -115,6 +126,11 @@ def test_near_maximal_lists(torch_gpu):
     idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
     log(f"  kept blocks per row: mean {cnt.mean():.1f}, max {cnt.max()} of {w.n_kblk}")
     assert cnt.mean() > 1500
+    users = np.zeros(w.n_kblk, int)
+    for i_ in range(w.n_qblk):
+        users[idx[0, 0, i_, :cnt[0, 0, i_]]] += 1
+    log(f"  query blocks per key block (head 0): mean {users.mean():.1f}, max {users.max()} "
+        f"of {w.n_qblk}")
     f = {n: O.widen_bf16(g[n][:, 0:1]) for n in ("q", "k", "v", "do")}
     mask = O.build_mask(f["q"], f["k"], w.blk_q, w.blk_k, w.k_frac, w.p)
     n, exempt, fails = parity.compare_mask_rows(idx[:, 0:1], cnt[:, 0:1], mask["rows"], w.p)
