@@ -1,4 +1,5 @@
-"""Compile the HIP sources of libspa.so for gfx950 with hipcc (in-tree build)."""
+"""Compile the HIP sources of libspa.so for gfx950 with hipcc (in-tree build), and the
+plain-C program that exercises its C ABI."""
 from __future__ import annotations
 
 import os
@@ -33,6 +34,30 @@ def _compile(src: str) -> str:
     return obj
 
 
+C_SMOKE_SRC = os.path.join(ROOT, "tests", "c", "abi_smoke.c")
+C_SMOKE_BIN = os.path.join(ROOT, "tests", "c", "abi_smoke")
+CC = os.environ.get("CC", "gcc")
+
+
+def build_c_smoke(verbose: bool = False) -> str:
+    """The plain-C program that drives the C ABI (no Python): linked against the in-tree
+    libspa.so (found through its run path) and the HIP runtime."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [CC, "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I" + os.path.join(rocm, "include"), "-I" + os.path.join(ROOT, "include"),
+           C_SMOKE_SRC, "-o", C_SMOKE_BIN + ".tmp", "-L" + PKG, "-lspa",
+           "-L" + os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/../../block_sparse_attention_pooled_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0 or r.stderr.strip():
+        raise RuntimeError(f"C smoke program failed to build cleanly:\n{r.stderr}")
+    os.replace(C_SMOKE_BIN + ".tmp", C_SMOKE_BIN)
+    if verbose:
+        print(f"built {C_SMOKE_BIN}")
+    return C_SMOKE_BIN
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
@@ -45,6 +70,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, OUT)
     if verbose:
         print(f"built {OUT}")
+    build_c_smoke(verbose)
     return OUT
 
 

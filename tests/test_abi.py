@@ -126,3 +126,15 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         spa.build_mask(q, q, 64, 64)
+
+
+def test_c_program_is_built_and_links():
+    """build() also produces tests/c/abi_smoke, a plain-C user of the ABI; its shared-library
+    dependencies (libspa.so through the run path, the HIP runtime) must resolve."""
+    import subprocess
+    binp = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "abi_smoke")
+    assert os.path.exists(binp), "run __graft_entry__.build() first"
+    r = subprocess.run(["ldd", binp], capture_output=True, text=True, timeout=30)
+    assert r.returncode == 0, r.stderr
+    assert "not found" not in r.stdout, r.stdout
+    assert "libspa.so" in r.stdout
