@@ -133,6 +133,8 @@ def main():
     dq, dk, dv = (torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
     mws = torch.empty(spa.mask_workspace_bytes(q.shape, w.blk_q, w.blk_k), dtype=torch.uint8,
                       device=dev)
+    fws = torch.empty(spa.fwd_workspace_bytes(q.shape, w.blk_q, w.blk_k), dtype=torch.uint8,
+                      device=dev)
     bws = torch.empty(spa.bwd_workspace_bytes(q.shape, w.blk_q, w.blk_k), dtype=torch.uint8,
                       device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -150,7 +152,7 @@ def main():
                        workspace=mws, stages=spa.MASK_SELECT)
         mark(2)
         spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k, with_residual=True,
-                            out=(o, lse, o_lo))
+                            out=(o, lse, o_lo), workspace=fws)
         mark(3)
         for st, idx in ((spa.BWD_PREP, 4), (spa.BWD_DQ, 5), (spa.BWD_DKDV, 6)):
             spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k, o_lo=o_lo,

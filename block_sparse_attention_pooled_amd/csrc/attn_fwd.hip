@@ -11,15 +11,19 @@
 // Per wavefront and tile:
 //   S^T = K Q^T   on v_mfma_f32_32x32x16_bf16 (K rows read in perm32 order, Q in
 //                 registers), so every lane holds 32 scores of a single query row;
-//   online softmax in fp32 with exp2; with o_lo requested the running maximum is
-//                 raised only when a tile's maximum exceeds it by more than 8 (log2
-//                 units), so most tiles skip the rescale of O (probabilities stay below
-//                 2^8);
-//   O^T += V^T P^T with V^T read by ds_read_b64_tr_b16; P enters the MFMA as bf16,
-//                 or, when the caller asks for the residual output o_lo, as a bf16
-//                 hi + lo pair so that O is accurate to about 16 bits (the backward
-//                 pass needs D = <dO, O> to that accuracy).
+//   online softmax in fp32 with exp2 against the exact running maximum, so that P <= 1
+//                 and a row's dominant probability is exactly 1;
+//   O^T += V^T P^T with V^T read by ds_read_b64_tr_b16.  P enters the MFMA as bf16, or,
+//                 when the caller asks for the residual output o_lo (the backward pass
+//                 needs D = <dO, O> to better than bf16), as one fp16 rounding against an
+//                 fp16 copy of V: fp16 carries three more mantissa bits than bf16, so O
+//                 is accurate to about 12 bits.  A workgroup whose list holds a key block of
+//                 V with a value that fp16 cannot carry (|v| >= 65504) reads bf16 V for all
+//                 its tiles instead, with P as a bf16 hi + lo pair (two MFMAs).
 // The row log-sum-exp is saved for the backward pass.
+//
+// k_vconv writes the fp16 copy of V for the residual mode, one workgroup per (b, h, key
+// block), with a per-block flag for blocks that fp16 cannot carry.
 #include "attn_tiles.h"
 #include "spa_internal.h"
 
@@ -28,9 +32,64 @@ namespace spa {
 
 #define SPA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// v_mfma_f32_32x32x16_f16, same lane layout as the bf16 form
+__device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// round-to-nearest-even of a float pair into packed fp16
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  const f32x2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
+}
+
+__device__ __forceinline__ f16x8 to_f16x8(const f32x16& x, int half) {
+  uint32_t w[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) w[t] = pk_f16(x[8 * half + 2 * t], x[8 * half + 2 * t + 1]);
+  return __builtin_bit_cast(f16x8, w);
+}
+
+// fp16 copy of one key block of V (rows at or beyond N are not written).  The conversion
+// is exact for bf16 values below 65504 in magnitude (fp16 has three more mantissa bits;
+// below 2^-14 it keeps an absolute 2^-25).  flag[bh][j] = 1 when the block holds a value
+// fp16 cannot carry (or a NaN), else 0: written on every call, so no clearing is needed.
+template <int D>
+__global__ __launch_bounds__(256) void k_vconv(const uint16_t* __restrict__ v,
+                                               uint16_t* __restrict__ v16, int N, int nkb,
+                                               int32_t* __restrict__ flag) {
+  constexpr int PER = kBlkK * D / 8 / 256;  // 16-byte chunks per thread
+  const int j = blockIdx.x, bh = blockIdx.y;
+  const int rows = min(kBlkK, N - j * kBlkK);
+  const size_t base = ((size_t)bh * N + (size_t)j * kBlkK) * D;
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int chunk = threadIdx.x + 256 * u;
+    if (chunk * 8 < rows * D) {
+      const uint4 a = *reinterpret_cast<const uint4*>(v + base + (size_t)chunk * 8);
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xFFFF0000u);
+        bad |= !(fabsf(x0) < 65504.f) || !(fabsf(x1) < 65504.f);
+        o[e] = pk_f16(x0, x1);
+      }
+      *reinterpret_cast<uint4*>(v16 + base + (size_t)chunk * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  const int any = __syncthreads_or(bad ? 1 : 0);
+  if (threadIdx.x == 0) flag[(size_t)bh * nkb + j] = any ? 1 : 0;
+}
+
 // One kept tile: S^T for this wave's 32 query rows, online softmax update, O^T += V^T P^T.
 // K and V rows at or beyond N were staged as zeros; their scores are masked here.
-template <int D, bool SPLIT, bool TAIL>
+template <int D, bool SPLIT, bool TAIL, bool V16>
 __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs, int key0, int N,
                                          const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
                                          float& m_run, float& l_run, float scale_log2, int lane) {
@@ -72,11 +131,9 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
 #pragma unroll
   for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sc[1][e]);
   mloc = fmaxf(mloc, swap_halves(mloc)) * scale_log2;
-  // With o_lo requested, P's rounding is carried by the lo half and the running maximum
-  // may lag the true one by up to 8 (log2 units).  Without it the maximum is exact, so the
-  // dominant probability of a peaked row is exactly 1 and rounds without error.
-  constexpr float kSlack = SPLIT ? 8.0f : 0.0f;
-  const bool raise = mloc > m_run + kSlack;
+  // the running maximum is exact: P <= 1, and the dominant probability of a peaked row is
+  // exactly 1, which every operand format carries without error
+  const bool raise = mloc > m_run;
   if (__ballot(raise)) {
     const float m_new = raise ? mloc : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -96,18 +153,30 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
   }
   l_run += psum;
   // ---- O^T += V^T P^T ---------------------------------------------------------------
+  if constexpr (SPLIT && V16) {  // the V tile holds fp16 bits; P as one fp16 rounding
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    bf16x8 ph, pl;
-    if constexpr (SPLIT)
-      split_bf16x8(sc[kk >> 1], kk & 1, ph, pl);
-    else
-      ph = to_bf16x8(sc[kk >> 1], kk & 1);
+    for (int kk = 0; kk < 4; ++kk) {
+      const f16x8 ph = to_f16x8(sc[kk >> 1], kk & 1);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const bf16x8 va = lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
-      oacc[db] = mfma32(va, ph, oacc[db]);
-      if constexpr (SPLIT) oacc[db] = mfma32(va, pl, oacc[db]);
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 va = lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
+        oacc[db] = mfma32h(__builtin_bit_cast(f16x8, va), ph, oacc[db]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 ph, pl;
+      if constexpr (SPLIT)
+        split_bf16x8(sc[kk >> 1], kk & 1, ph, pl);
+      else
+        ph = to_bf16x8(sc[kk >> 1], kk & 1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 va = lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
+        oacc[db] = mfma32(va, ph, oacc[db]);
+        if constexpr (SPLIT) oacc[db] = mfma32(va, pl, oacc[db]);
+      }
     }
   }
 }
@@ -116,6 +185,8 @@ template <int D, int BQ, bool SPLIT>
 __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ q,
                                                   const uint16_t* __restrict__ k,
                                                   const uint16_t* __restrict__ v,
+                                                  const uint16_t* __restrict__ v16,
+                                                  const int32_t* __restrict__ vflag,
                                                   const int32_t* __restrict__ kv_idx,
                                                   const int32_t* __restrict__ kv_cnt, int N,
                                                   int nqb, int nkb, int total, float scale_log2,
@@ -136,10 +207,18 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   const size_t head = (size_t)bh * N * D;
   const u32x4 krs = make_rsrc(k + head, (uint32_t)N * D * 2);
   const u32x4 vrs = make_rsrc(v + head, (uint32_t)N * D * 2);
+  const u32x4 v16rs = SPLIT ? make_rsrc(v16 + head, (uint32_t)N * D * 2) : vrs;
   const int32_t* list = kv_idx + ((size_t)bh * nqb + i) * nkb;
   // the lists are trusted; the clamp only keeps a corrupt count inside the LDS list
   const int cnt = min(max(kv_cnt[(size_t)bh * nqb + i], 0), nkb);
-  for (int x = threadIdx.x; x < cnt; x += NT) lst[x] = list[x];
+  int bad16 = 0;
+  for (int x = threadIdx.x; x < cnt; x += NT) {
+    const int j = list[x];
+    lst[x] = j;
+    if (SPLIT) bad16 |= vflag[(size_t)bh * nkb + min(max(j, 0), nkb - 1)];
+  }
+  // one operand format for the whole workgroup: fp16 V unless a listed block cannot use it
+  const bool use16 = SPLIT && !__syncthreads_or(bad16);
 
   // this lane's query row (B operand of S^T = K Q^T); rows beyond N compute on a copy of
   // row N-1 and are never written
@@ -157,34 +236,40 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
 
   __syncthreads();  // list staged
   auto blk = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[min(t, cnt - 1)]); };
+  const u32x4 vsrc = use16 ? v16rs : vrs;
   if (cnt > 0) {
     const int j0 = blk(0);
     tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0]);
-    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, j0 * kBlkK, smem[0][1]);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vsrc, j0 * kBlkK, smem[0][1]);
   }
   wait_vmem();  // also the Q fragments: nothing vector-memory is pending inside the loop
   __syncthreads();
-  // only the last key block of the list can be partial: it gets its own instantiation of
-  // the tile body after the loop, so that the loop carries no per-element selects
   const bool tail_last = cnt > 0 && blk(cnt - 1) * kBlkK + kBlkK > N;
   const int cnt_main = cnt - (tail_last ? 1 : 0);
-  for (int t = 0; t < cnt_main; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < cnt) {  // the next tile streams into the other buffer meanwhile
-      const int jn = blk(t + 1);
-      tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0]);
-      tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, jn * kBlkK, smem[buf ^ 1][1]);
-    }
-    fwd_tile<D, SPLIT, false>(smem[buf][0], smem[buf][1], blk(t) * kBlkK, N, qf, oacc, m_run,
-                              l_run, scale_log2, lane);
-    wait_vmem();
-    __syncthreads();
+#define SPA_FWD_LOOP(V16_)                                                                   \
+  {                                                                                        \
+    for (int t = 0; t < cnt_main; ++t) {                                                   \
+      const int buf = t & 1;                                                               \
+      if (t + 1 < cnt) {                                                                   \
+        const int jn = blk(t + 1);                                                         \
+        tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0]);          \
+        tile_load_lds_rsrc<D, kBlkK, NT / 64>(vsrc, jn * kBlkK, smem[buf ^ 1][1]);         \
+      }                                                                                    \
+      fwd_tile<D, SPLIT, false, V16_>(smem[buf][0], smem[buf][1], blk(t) * kBlkK, N, qf,   \
+                                      oacc, m_run, l_run, scale_log2, lane);               \
+      wait_vmem();                                                                         \
+      __syncthreads();                                                                     \
+    }                                                                                      \
+    if (tail_last) {                                                                       \
+      const int buf = cnt_main & 1;                                                        \
+      fwd_tile<D, SPLIT, true, V16_>(smem[buf][0], smem[buf][1], blk(cnt_main) * kBlkK, N, \
+                                     qf, oacc, m_run, l_run, scale_log2, lane);            \
+    }                                                                                      \
   }
-  if (tail_last) {
-    const int buf = cnt_main & 1;
-    fwd_tile<D, SPLIT, true>(smem[buf][0], smem[buf][1], blk(cnt_main) * kBlkK, N, qf, oacc,
-                             m_run, l_run, scale_log2, lane);
-  }
+  // two copies of the loop, one per operand format, so that neither carries the other's
+  // registers
+  if (use16) SPA_FWD_LOOP(true) else SPA_FWD_LOOP(false)
+#undef SPA_FWD_LOOP
 
   // ---- epilogue ---------------------------------------------------------------------
   const float l_tot = l_run + swap_halves(l_run);
@@ -216,13 +301,29 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   const Geometry& g = a.g;
   const int total = (int)(g.nqb * g.bh());
   dim3 grid(total);
-  if (a.o_lo)
-    hipLaunchKernelGGL((k_fwd<D, BQ, true>), grid, dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.kv_idx,
-                       a.kv_cnt, g.N, g.nqb, g.nkb, total, a.scale * kLog2e, a.o, a.o_lo, a.lse);
-  else
-    hipLaunchKernelGGL((k_fwd<D, BQ, false>), grid, dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.kv_idx,
-                       a.kv_cnt, g.N, g.nqb, g.nkb, total, a.scale * kLog2e, a.o, a.o_lo, a.lse);
+  if (a.o_lo) {
+    hipLaunchKernelGGL((k_vconv<D>), dim3(g.nkb, (unsigned)g.bh()), dim3(256), 0, s, a.v, a.v16,
+                       g.N, g.nkb, a.vflag);
+    hipLaunchKernelGGL((k_fwd<D, BQ, true>), grid, dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.v16,
+                       a.vflag, a.kv_idx, a.kv_cnt, g.N, g.nqb, g.nkb, total, a.scale * kLog2e,
+                       a.o, a.o_lo, a.lse);
+  } else {
+    hipLaunchKernelGGL((k_fwd<D, BQ, false>), grid, dim3(BQ * 2), 0, s, a.q, a.k, a.v,
+                       (const uint16_t*)nullptr, (const int32_t*)nullptr, a.kv_idx, a.kv_cnt,
+                       g.N, g.nqb, g.nkb, total, a.scale * kLog2e, a.o, a.o_lo, a.lse);
+  }
   return hipGetLastError();
+}
+
+size_t fwd_workspace_bytes(const Geometry& g) {
+  return align_up((size_t)g.bh() * g.N * g.d * 2, 256) + align_up((size_t)g.bh() * g.nkb * 4, 256);
+}
+
+void fwd_workspace_carve(const Geometry& g, void* ws, FwdArgs* a) {
+  char* p = static_cast<char*>(ws);
+  a->v16 = reinterpret_cast<uint16_t*>(p);
+  p += align_up((size_t)g.bh() * g.N * g.d * 2, 256);
+  a->vflag = reinterpret_cast<int32_t*>(p);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {

@@ -89,15 +89,26 @@ int spa_build_mask_stages(const spa_dims* dims, const void* q, const void* k, do
   return launch_status(spa::launch_mask(a, stages, static_cast<hipStream_t>(stream)));
 }
 
+size_t spa_fwd_workspace_bytes(const spa_dims* dims) {
+  Geometry g;
+  if (check_dims(dims, &g) != SPA_OK) return 0;
+  return spa::fwd_workspace_bytes(g);
+}
+
 int spa_sparse_attn_fwd(const spa_dims* dims, const void* q, const void* k, const void* v,
                         const int32_t* kv_idx, const int32_t* kv_cnt, double scale, void* o,
-                        void* o_lo, float* lse, void* stream) {
+                        void* o_lo, float* lse, void* ws, size_t ws_bytes, void* stream) {
   Geometry g;
   int rc = check_dims(dims, &g);
   if (rc != SPA_OK) return rc;
   if (!q || !k || !v || !kv_idx || !kv_cnt || !o || !lse) return SPA_E_NULL;
+  if (o_lo && !ws) return SPA_E_NULL;
   if (std::isnan(scale) || std::isinf(scale)) return SPA_E_PARAM;
+  if (o_lo && ws_bytes < spa::fwd_workspace_bytes(g)) return SPA_E_WORKSPACE;
   spa::FwdArgs a;
+  a.v16 = nullptr;
+  a.vflag = nullptr;
+  if (o_lo) spa::fwd_workspace_carve(g, ws, &a);
   a.g = g;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);

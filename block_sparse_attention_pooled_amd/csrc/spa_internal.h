@@ -45,7 +45,11 @@ struct FwdArgs {
   uint16_t* o;
   uint16_t* o_lo;  // may be null
   float* lse;
+  uint16_t* v16;   // workspace (with o_lo): fp16 copy of V [BH][N][d]
+  int32_t* vflag;  // workspace (with o_lo): [BH][Nkb], 1 where fp16 cannot carry the block
 };
+size_t fwd_workspace_bytes(const Geometry& g);
+void fwd_workspace_carve(const Geometry& g, void* ws, FwdArgs* a);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
 
 // ---- backward -----------------------------------------------------------------------

@@ -112,17 +112,27 @@ SPA_API int spa_build_mask(const spa_dims* dims, const void* q, const void* k, d
  *                 unique, within [0, Nkb) and non-empty (they are trusted).
  *   scale         softmax scale; <= 0 selects 1/sqrt(d).
  *   o             bf16 [B, H, N, d] device, out: O rounded to nearest even.
- *   o_lo          bf16 [B, H, N, d] device, out, or NULL: the rounding residual, so that
- *                 o + o_lo carries O to about 16 significant bits.  Request it when a
- *                 backward pass follows: the gradients depend on D = <dO, O> to first
- *                 order, and bf16 O alone leaves D off by about 2^-9 |dO| |O|.  With
- *                 o_lo the probabilities enter P*V as a bf16 hi + lo pair (one more MFMA
- *                 per product); without it, as bf16.
+ *   o_lo          bf16 [B, H, N, d] device, out, or NULL: the rounding residual of O.
+ *                 Request it when a backward pass follows: the gradients depend on
+ *                 D = <dO, O> to first order, and bf16 O alone leaves D off by about
+ *                 2^-9 |dO| |O|.  With o_lo the probabilities enter P*V as one fp16
+ *                 rounding against an fp16 copy of V (fp16 has three more mantissa bits
+ *                 than bf16), so o + o_lo carries O to about 12 significant bits.  A query
+ *                 block whose list holds a key block of V with a value of magnitude 65504
+ *                 or more (beyond fp16) takes bf16 V with P as a bf16 hi + lo pair
+ *                 instead (about 16 bits).  Without o_lo, P enters as bf16.
  *   lse           fp32 [B, H, N] device, out (natural log).
+ *   ws, ws_bytes  device workspace of at least spa_fwd_workspace_bytes(dims) when o_lo is
+ *                 given (the fp16 copy of V and a flag per key block); ignored, and may be
+ *                 NULL, without o_lo.
  */
 SPA_API int spa_sparse_attn_fwd(const spa_dims* dims, const void* q, const void* k, const void* v,
                         const int32_t* kv_idx, const int32_t* kv_cnt, double scale, void* o,
-                        void* o_lo, float* lse, void* stream);
+                        void* o_lo, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace spa_sparse_attn_fwd needs with o_lo (an fp16 copy of V and
+ * one int32 flag per key block, 256-byte aligned sections).  0 for rejected dims. */
+SPA_API size_t spa_fwd_workspace_bytes(const spa_dims* dims);
 
 /* Bytes of device workspace spa_sparse_attn_bwd needs (D = rowsum(dO*O) and lse*log2(e)
  * per row, padded to whole query blocks, the kept-tile

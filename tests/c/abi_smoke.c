@@ -127,8 +127,15 @@ int main(int argc, char** argv) {
   void* o = dev_alloc(nel * 2);
   void* o_lo = dev_alloc(nel * 2);
   float* lse = (float*)dev_alloc(nrow * 4);
-  EXPECT(spa_sparse_attn_fwd(&dm, q, k, v, kv_idx, kv_cnt, 0.0, o, o_lo, lse, NULL) == SPA_OK,
-         "sparse_attn_fwd");
+  const size_t fws_bytes = spa_fwd_workspace_bytes(&dm);
+  EXPECT(fws_bytes > 0, "fwd workspace size");
+  void* fws = dev_alloc(fws_bytes);
+  EXPECT(spa_sparse_attn_fwd(&dm, q, k, v, kv_idx, kv_cnt, 0.0, o, o_lo, lse, NULL, 0, NULL) ==
+             SPA_E_NULL, "the residual output needs the workspace");
+  EXPECT(spa_sparse_attn_fwd(&dm, q, k, v, kv_idx, kv_cnt, 0.0, o, o_lo, lse, fws, fws_bytes - 1,
+                             NULL) == SPA_E_WORKSPACE, "short forward workspace is rejected");
+  EXPECT(spa_sparse_attn_fwd(&dm, q, k, v, kv_idx, kv_cnt, 0.0, o, o_lo, lse, fws, fws_bytes,
+                             NULL) == SPA_OK, "sparse_attn_fwd");
   const size_t bws_bytes = spa_bwd_workspace_bytes(&dm);
   EXPECT(bws_bytes > 0, "bwd workspace size");
   void* bws = dev_alloc(bws_bytes);
@@ -177,7 +184,7 @@ int main(int argc, char** argv) {
   for (int t = 0; t < 3; ++t) fwrite(h_g[t], 4, nel, f);
   fclose(f);
 
-  void* dev_bufs[] = {q, k, v, dout, kv_idx, kv_cnt, mws, o, o_lo, lse, bws, dq, dk, dv};
+  void* dev_bufs[] = {q, k, v, dout, kv_idx, kv_cnt, mws, o, o_lo, lse, fws, bws, dq, dk, dv};
   for (size_t i = 0; i < sizeof(dev_bufs) / sizeof(dev_bufs[0]); ++i)
     CHECK_HIP(hipFree(dev_bufs[i]));
   printf("abi_smoke ok: %d x %d lists, version %d\n", (int)nlist, nkb, spa_version());

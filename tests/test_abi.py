@@ -59,6 +59,14 @@ def test_bwd_workspace_size_formula():
     assert want <= got <= want + 1024
 
 
+def test_fwd_workspace_size_formula():
+    B, H, N, d = 2, 3, 1000, 128
+    nkb = -(-N // 64)
+    al = lambda x: -(-x // 256) * 256
+    want = al(B * H * N * d * 2) + al(B * H * nkb * 4)  # fp16 copy of V, flag per key block
+    assert spa.fwd_workspace_bytes((B, H, N, d), 128, 64) == want
+
+
 @pytest.mark.parametrize("dims,code", [
     (dict(B=0), -2), (dict(N=0), -2), (dict(d=96), -4), (dict(bq=32), -4), (dict(bk=128), -4),
     (dict(N=64 * 2049), -4), (dict(B=1, H=64, N=300000, d=128), -2),
@@ -68,11 +76,12 @@ def test_bad_dims_rejected(dims, code):
     d = _dims(**dims)
     assert lib.spa_mask_workspace_bytes(ctypes.byref(d)) == 0
     assert lib.spa_bwd_workspace_bytes(ctypes.byref(d)) == 0
+    assert lib.spa_fwd_workspace_bytes(ctypes.byref(d)) == 0
     rc = lib.spa_build_mask(ctypes.byref(d), FAKE, FAKE, 0.05, 0.9, 0.0, FAKE, FAKE, None,
                             FAKE, 1 << 40, None)
     assert rc == code
     rc = lib.spa_sparse_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, None,
-                                 FAKE, None)
+                                 FAKE, None, 0, None)
     assert rc == code
 
 
@@ -84,7 +93,10 @@ def test_null_pointers_rejected():
     assert lib.spa_build_mask(ctypes.byref(d), None, FAKE, 0.05, 0.9, 0.0, FAKE, FAKE, None, FAKE,
                               1 << 40, None) == -1
     assert lib.spa_sparse_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, None,
-                                   None, None) == -1
+                                   None, None, 0, None) == -1
+    # the residual output needs the workspace
+    assert lib.spa_sparse_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, FAKE,
+                                   FAKE, None, 1 << 40, None) == -1
     assert lib.spa_sparse_attn_bwd(ctypes.byref(d), *([FAKE] * 5), None, FAKE, FAKE, FAKE,
                                    0.0, FAKE, FAKE, None, 0, FAKE, 1 << 40, None) == -1
 
@@ -103,7 +115,7 @@ def test_bad_scales_and_grad_dtype_rejected():
     lib = spa.load_library()
     d = _dims()
     assert lib.spa_sparse_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, float("inf"),
-                                   FAKE, None, FAKE, None) == -3
+                                   FAKE, None, FAKE, None, 0, None) == -3
     assert lib.spa_build_mask(ctypes.byref(d), FAKE, FAKE, 0.05, 0.9, float("nan"), FAKE, FAKE,
                               None, FAKE, 1 << 40, None) == -3
     assert lib.spa_sparse_attn_bwd(ctypes.byref(d), *([FAKE] * 9), 0.0, FAKE, FAKE, FAKE, 2, FAKE,
@@ -119,6 +131,9 @@ def test_small_workspace_rejected():
     need = lib.spa_bwd_workspace_bytes(ctypes.byref(d))
     assert lib.spa_sparse_attn_bwd(ctypes.byref(d), *([FAKE] * 9), 0.0, FAKE, FAKE, FAKE, 0, FAKE,
                                    need - 1, None) == -5
+    need = lib.spa_fwd_workspace_bytes(ctypes.byref(d))
+    assert lib.spa_sparse_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, FAKE,
+                                   FAKE, FAKE, need - 1, None) == -5
 
 
 def test_python_binding_refuses_cpu_tensors():
