@@ -15,11 +15,14 @@
 //               ascending order, recomputes S and P (reading D and lse * log2(e) that k_dq
 //               wrote), accumulates dV += P^T dO and dK += dS^T Q in registers (no atomics,
 //               fixed order).
-// All products are bf16 MFMA with fp32 accumulation.  P (in dV = P^T dO) and dS (in
-// dQ = dS K and dK = dS^T Q) enter as bf16 hi + lo pairs (about 16 bits): on peaked
-// rows dS is a difference of nearly equal terms, and dV of a key that many queries
-// attend to sums thousands of products, so a single bf16 rounding of either would be
-// visible in the gradients.
+// All products are MFMA with fp32 accumulation.  dS (in dQ = dS K and dK = dS^T Q) enters
+// as a bf16 hi + lo pair (about 16 bits): on peaked rows dS is a difference of nearly
+// equal terms, and a single bf16 rounding would be visible in the gradients.  P (in
+// dV = P^T dO, where a key that many queries attend to sums thousands of products) enters
+// as one fp16 rounding (P <= 1) against an fp16 copy of dO that k_dq writes; a key block
+// whose list holds a query block with dO beyond fp16's range, or whose V is beyond it,
+// takes bf16 dO with P as a bf16 hi + lo pair.  dP = dO V^T runs on the same operand
+// format as dO (V converted in registers; both conversions are exact).
 #include "attn_tiles.h"
 #include "spa_internal.h"
 
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
 // The 64 keys x 64 rows of a stage split into four units (32 keys x 32 rows).  Each
 // unit has two wavefronts with different jobs, placed so that they share a SIMD:
 //   producer (waves 0-3):  S = Q K^T (K fragments in registers), P = exp2(S c - lse2),
-//                          P to LDS (fp32), dV += P^T dO with P as a bf16 hi + lo pair;
+//                          P to LDS (fp32), dV += P^T dO (P in fp16, or a bf16 pair);
 //   consumer (waves 4-7):  one stage behind: dP = dO V^T (V fragments in registers),
 //                          P from LDS, dS = P (dP - D), dK += dS^T Q with dS as a bf16
 //                          hi + lo pair.
@@ -172,6 +175,25 @@ __device__ __forceinline__ void dkdv_dv(const uint16_t* tq, const f32x16& p, f32
   }
 }
 
+// Producer, second half, fp16 form: dV += P^T dO with P as one fp16 rounding (P <= 1)
+// against the fp16 copy of dO held in the stage slot.
+template <int D>
+__device__ __forceinline__ void dkdv_dv16(const uint16_t* tq, const f32x16& p,
+                                          f32x16 (&acc)[D / 32], int r0, int lane) {
+  constexpr int DB = D / 32, HR = 64;
+  const uint16_t* dOb = tq + HR * D;
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq) {
+    bf16x8 ob[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) ob[db] = lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
+    const f16x8 ph = to_f16x8(p, kq);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      acc[db] = mfma32h(ph, __builtin_bit_cast(f16x8, ob[db]), acc[db]);
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void dkdv_rowfrags(const uint16_t* tile, int r0, int lane,
                                               bf16x8 (&a)[D / 16]) {
@@ -187,6 +209,17 @@ __device__ __forceinline__ void dkdv_dp(const bf16x8 (&a)[D / 16], const bf16x8 
   dp = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) dp = mfma32(a[kk], vf[kk], dp);
+}
+
+// The same with fp16 dO rows and fp16 V (both exact conversions of the bf16 data).
+template <int D>
+__device__ __forceinline__ void dkdv_dp16(const bf16x8 (&a)[D / 16], const bf16x8 (&vf)[D / 16],
+                                          f32x16& dp) {
+  constexpr int KS = D / 16;
+  dp = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    dp = mfma32h(__builtin_bit_cast(f16x8, a[kk]), __builtin_bit_cast(f16x8, vf[kk]), dp);
 }
 
 // Consumer, second half: dS = P (dP - D) with P from the producer, dK += dS^T Q.
@@ -236,7 +269,8 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
     const float* __restrict__ lse2p, const float* __restrict__ dsum,
     const int32_t* __restrict__ q_idx, const int32_t* __restrict__ q_cnt, int N, int npad,
     int nqb, int nkb, int total, float scale_log2, float scale, void* __restrict__ dk_out,
-    void* __restrict__ dv_out, int grad_bf16) {
+    void* __restrict__ dv_out, int grad_bf16, const uint16_t* __restrict__ do16,
+    const int32_t* __restrict__ doflag) {
   constexpr int DB = D / 32;
   constexpr int KS = D / 16;
   constexpr int HR = 64;                 // query rows per stage
@@ -248,6 +282,7 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   // the query-block list, staged once: reading it from LDS keeps scalar loads (which
   // complete out of order) out of the loop, so LDS waits can stay partial
   __shared__ int32_t lst[kMaxBlocks];
+  __shared__ uint32_t wbits[8];  // per wavefront: fp16 range classes of V, listed dO flags
   static_assert(2 * DB * 16 * 64 * 4 <= SLOT * 2, "reduction buffer reuses a slot");
 
   const int tile_id = xcd_remap(blockIdx.x, total);
@@ -269,7 +304,10 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   const int nst = cnt * HPB;
   DkdvSrc src;
   src.q = make_rsrc(q + head, (uint32_t)N * D * 2);
-  src.dout = make_rsrc(dout + head, (uint32_t)N * D * 2);
+  // dO is staged from its fp16 copy unless a listed query block's dO, or this key
+  // block's V, is not to be read through fp16 (f16_block_ok): then from bf16 dO, with P
+  // as a bf16 pair
+  src.dout = make_rsrc(do16 + head, (uint32_t)N * D * 2);
   src.lse2 = make_rsrc(lse2p + (size_t)bh * npad, (uint32_t)npad * 4);
   src.dsum = make_rsrc(dsum + (size_t)bh * npad, (uint32_t)npad * 4);
   for (int x = threadIdx.x; x < cnt; x += 512) lst[x] = list[x];
@@ -277,6 +315,9 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   auto list_at = [&](int st) {
     return __builtin_amdgcn_readfirstlane(lst[max(0, min(st / HPB, cnt - 1))]);
   };
+  uint32_t rbits = 0;  // bit 3: a listed dO block is flagged; bits 0-2: V range classes
+  for (int x = threadIdx.x; x < cnt; x += 512)
+    rbits |= doflag[(size_t)bh * nqb + lst[x]] != 0 ? 8u : 0u;
   if (nst > 0) dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tiles[0], side[0]);
 
   bf16x8 bf[KS];  // producer: K row of this lane's key; consumer: V row
@@ -289,7 +330,23 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   wait_vmem();  // stage 0 and the K / V fragments: nothing of the compiler's is pending
+  if (role == 1) {  // the consumer waves hold all of this key block's V between them
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) rbits |= f16_range_bits(__builtin_bit_cast(uint4, bf[kk]));
+  }
+  rbits = wave_or4(rbits);
+  if (lane == 0) wbits[w] = rbits;
   __syncthreads();
+  uint32_t all = 0;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) all |= wbits[x];
+  const bool use16 = !(all & 8u) && f16_block_ok(all & 7u);
+  if (!use16) {  // stage 0 again, from bf16 dO
+    src.dout = make_rsrc(dout + head, (uint32_t)N * D * 2);
+    if (nst > 0) dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tiles[0], side[0]);
+    wait_vmem();
+    __syncthreads();
+  }
 
   // One step: loads of stage st+1 into the next slot, producer on stage st, consumer on
   // stage st-1.  Each job runs its own copy of the loop (same barriers), so that neither
@@ -308,7 +365,36 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
       cur = nxt;                                                                           \
     }                                                                                      \
   }
-  if (role == 0 && tail) {  // keys at or beyond N exist only in the last key block
+  if (use16) {
+    if (role == 0 && tail) {
+      SPA_DKDV_LOOP(if (st < nst) {
+        f32x16 p;
+        dkdv_scores<D, true>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane,
+                             kmask, scale_log2, p);
+        dkdv_dv16<D>(tiles[cur], p, acc, r0, lane);
+      })
+    } else if (role == 0) {
+      SPA_DKDV_LOOP(if (st < nst) {
+        f32x16 p;
+        dkdv_scores<D, false>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane,
+                              kmask, scale_log2, p);
+        dkdv_dv16<D>(tiles[cur], p, acc, r0, lane);
+      })
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)  // V to fp16 (checked above)
+        bf[kk] = __builtin_bit_cast(bf16x8, bf16x8_bits_to_f16(__builtin_bit_cast(uint4, bf[kk])));
+      SPA_DKDV_LOOP(if (st >= 1) {
+        bf16x8 a[KS];
+        dkdv_rowfrags<D>(tiles[prev] + HR * D, r0, lane, a);
+        SPA_FENCE();
+        f32x16 dp;
+        dkdv_dp16<D>(a, bf, dp);
+        dkdv_dk<D>(tiles[prev], side[prev], pbuf[(st - 1) & 1] + unit * 1024, dp, acc, r0,
+                   lane);
+      })
+    }
+  } else if (role == 0 && tail) {  // keys at or beyond N exist only in the last key block
     SPA_DKDV_LOOP(if (st < nst) {
       f32x16 p;
       dkdv_scores<D, true>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane,
@@ -458,12 +544,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     const float* __restrict__ lse, float* __restrict__ lse2p, float* __restrict__ dsum,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int N, int npad,
     int nqb, int nkb, int total, float scale_log2, float scale, void* __restrict__ dq_out,
-    int grad_bf16) {
+    int grad_bf16, uint16_t* __restrict__ do16, int32_t* __restrict__ doflag) {
   constexpr int NT = BQ * 2;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   __shared__ __align__(16) uint16_t smem[2][2][Tile<D>::ELEMS];  // [buf][K|V]
   __shared__ int32_t lst[kMaxBlocks];  // the key-block list (keeps scalar loads out of the loop)
+  __shared__ uint32_t wbits[NT / 64];  // fp16 range classes of dO, per wavefront
 
   const int tile_id = xcd_remap(blockIdx.x, total);
   const int bh = tile_id / nqb;
@@ -495,12 +582,32 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     lse2p[ri] = lse2;
     dsum[ri] = dq_sum;
   }
+  // the fp16 copy of this block's dO rows for k_dkdv's dV = P^T dO, and a flag when the
+  // block is not to be read through it (f16_block_ok; k_dkdv then reads bf16 dO for every
+  // block of its list)
+  uint32_t rbits = 0;
+  if (qvalid) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 u = __builtin_bit_cast(uint4, df[kk]);
+      rbits |= f16_range_bits(u);
+      *reinterpret_cast<uint4*>(do16 + qoff + 16 * kk) = bf16x8_bits_to_f16(u);
+    }
+  }
+  rbits = wave_or4(rbits);
+  if (lane == 0) wbits[wv] = rbits;
 
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  __syncthreads();  // list staged
+  __syncthreads();  // list and range bits staged
+  if (threadIdx.x == 0) {
+    uint32_t all = 0;
+#pragma unroll
+    for (int x = 0; x < NT / 64; ++x) all |= wbits[x];
+    doflag[(size_t)bh * nqb + i] = f16_block_ok(all) ? 0 : 1;
+  }
   if (cnt > 0) {
     const int j0 = blk(0);
     tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0]);
@@ -561,7 +668,9 @@ size_t bwd_workspace_bytes(const Geometry& g) {
   return 2 * align_up(bh * n_pad(g) * sizeof(float), 256) +
          align_up(bh * n_words(g) * g.nqb * sizeof(uint32_t), 256) +
          align_up(bh * g.nkb * g.nqb * sizeof(int32_t), 256) +
-         align_up(bh * g.nkb * sizeof(int32_t), 256);
+         align_up(bh * g.nkb * sizeof(int32_t), 256) +
+         align_up(bh * (size_t)g.N * g.d * sizeof(uint16_t), 256) +
+         align_up(bh * g.nqb * sizeof(int32_t), 256);
 }
 
 void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a) {
@@ -576,6 +685,10 @@ void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a) {
   a->q_idx = reinterpret_cast<int32_t*>(p);
   p += align_up(bh * g.nkb * g.nqb * sizeof(int32_t), 256);
   a->q_cnt = reinterpret_cast<int32_t*>(p);
+  p += align_up(bh * g.nkb * sizeof(int32_t), 256);
+  a->do16 = reinterpret_cast<uint16_t*>(p);
+  p += align_up(bh * (size_t)g.N * g.d * sizeof(uint16_t), 256);
+  a->doflag = reinterpret_cast<int32_t*>(p);
 }
 
 template <int D, int BQ>
@@ -594,13 +707,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
     const int total = (int)(g.nqb * g.bh());
     hipLaunchKernelGGL((k_dq<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.o,
                        a.o_lo, a.dout, a.lse, a.lse2, a.dsum, a.kv_idx, a.kv_cnt, g.N, npad,
-                       g.nqb, g.nkb, total, sl2, a.scale, a.dq, a.grad_bf16);
+                       g.nqb, g.nkb, total, sl2, a.scale, a.dq, a.grad_bf16, a.do16,
+                       a.doflag);
   }
   if (stages & 4u) {
     const int total = (int)(g.nkb * g.bh());
     hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(total), dim3(512), 0, s, a.q, a.k, a.v, a.dout,
                        a.lse2, a.dsum, a.q_idx, a.q_cnt, g.N, npad, g.nqb, g.nkb, total, sl2,
-                       a.scale, a.dk, a.dv, a.grad_bf16);
+                       a.scale, a.dk, a.dv, a.grad_bf16, a.do16, a.doflag);
   }
   return hipGetLastError();
 }

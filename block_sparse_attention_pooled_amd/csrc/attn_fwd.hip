@@ -18,12 +18,14 @@
 //                 needs D = <dO, O> to better than bf16), as one fp16 rounding against an
 //                 fp16 copy of V: fp16 carries three more mantissa bits than bf16, so O
 //                 is accurate to about 12 bits.  A workgroup whose list holds a key block of
-//                 V with a value that fp16 cannot carry (|v| >= 65504) reads bf16 V for all
-//                 its tiles instead, with P as a bf16 hi + lo pair (two MFMAs).
+//                 V that fp16 cannot carry (a value with |v| >= 65504, or only small values
+//                 that fp16 would keep to less than 2^-16 of the block's largest) reads
+//                 bf16 V for all its tiles instead, with P as a bf16 hi + lo pair (two
+//                 MFMAs).
 // The row log-sum-exp is saved for the backward pass.
 //
 // k_vconv writes the fp16 copy of V for the residual mode, one workgroup per (b, h, key
-// block), with a per-block flag for blocks that fp16 cannot carry.
+// block), with a per-block flag for blocks that are not to be read through it.
 #include "attn_tiles.h"
 #include "spa_internal.h"
 
@@ -32,59 +34,34 @@ namespace spa {
 
 #define SPA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
-typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-
-// v_mfma_f32_32x32x16_f16, same lane layout as the bf16 form
-__device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// round-to-nearest-even of a float pair into packed fp16
-__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
-  const f32x2v v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
-}
-
-__device__ __forceinline__ f16x8 to_f16x8(const f32x16& x, int half) {
-  uint32_t w[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) w[t] = pk_f16(x[8 * half + 2 * t], x[8 * half + 2 * t + 1]);
-  return __builtin_bit_cast(f16x8, w);
-}
-
-// fp16 copy of one key block of V (rows at or beyond N are not written).  The conversion
-// is exact for bf16 values below 65504 in magnitude (fp16 has three more mantissa bits;
-// below 2^-14 it keeps an absolute 2^-25).  flag[bh][j] = 1 when the block holds a value
-// fp16 cannot carry (or a NaN), else 0: written on every call, so no clearing is needed.
+// fp16 copy of one key block of V (rows at or beyond N are not written).  flag[bh][j] = 1
+// when the block is not to be read through the copy (a value beyond fp16's range, or
+// small values that fp16 would carry to less than 2^-16 of the block's largest; see
+// f16_block_ok), else 0: written on every call, so no clearing is needed.
 template <int D>
 __global__ __launch_bounds__(256) void k_vconv(const uint16_t* __restrict__ v,
                                                uint16_t* __restrict__ v16, int N, int nkb,
                                                int32_t* __restrict__ flag) {
   constexpr int PER = kBlkK * D / 8 / 256;  // 16-byte chunks per thread
+  __shared__ uint32_t wbits[4];
   const int j = blockIdx.x, bh = blockIdx.y;
   const int rows = min(kBlkK, N - j * kBlkK);
   const size_t base = ((size_t)bh * N + (size_t)j * kBlkK) * D;
-  bool bad = false;
+  uint32_t r = 0;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int chunk = threadIdx.x + 256 * u;
     if (chunk * 8 < rows * D) {
       const uint4 a = *reinterpret_cast<const uint4*>(v + base + (size_t)chunk * 8);
-      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xFFFF0000u);
-        bad |= !(fabsf(x0) < 65504.f) || !(fabsf(x1) < 65504.f);
-        o[e] = pk_f16(x0, x1);
-      }
-      *reinterpret_cast<uint4*>(v16 + base + (size_t)chunk * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+      r |= f16_range_bits(a);
+      *reinterpret_cast<uint4*>(v16 + base + (size_t)chunk * 8) = bf16x8_bits_to_f16(a);
     }
   }
-  const int any = __syncthreads_or(bad ? 1 : 0);
-  if (threadIdx.x == 0) flag[(size_t)bh * nkb + j] = any ? 1 : 0;
+  const uint32_t wr = wave_or4(r);
+  if ((threadIdx.x & 63) == 0) wbits[threadIdx.x >> 6] = wr;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    flag[(size_t)bh * nkb + j] = f16_block_ok(wbits[0] | wbits[1] | wbits[2] | wbits[3]) ? 0 : 1;
 }
 
 // One kept tile: S^T for this wave's 32 query rows, online softmax update, O^T += V^T P^T.

@@ -156,6 +156,78 @@ __device__ __forceinline__ void split_bf16x8(const f32x16& x, int half, bf16x8& 
   lo = __builtin_bit_cast(bf16x8, wl);
 }
 
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+
+// v_mfma_f32_32x32x16_f16, same lane layout as the bf16 form
+__device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// round-to-nearest-even of a float pair into packed fp16
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
+}
+
+__device__ __forceinline__ f16x8 to_f16x8(const f32x16& x, int half) {
+  uint32_t w[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) w[t] = pk_f16(x[8 * half + 2 * t], x[8 * half + 2 * t + 1]);
+  return __builtin_bit_cast(f16x8, w);
+}
+
+// Eight bf16 values (packed in a uint4) as fp16 bit patterns, round to nearest even.
+// Exact for magnitudes from 2^-14 to below 65504 (fp16 has three more mantissa bits than
+// bf16); below 2^-14 fp16 keeps an absolute 2^-25.
+__device__ __forceinline__ uint4 bf16x8_bits_to_f16(const uint4& a) {
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = pk_f16(__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xFFFF0000u));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Range classes of eight bf16 values (packed in a uint4) for an fp16 copy, OR-ed together:
+//   kF16Over  a value fp16 cannot carry (|x| >= 65504, an infinity or a NaN);
+//   kF16Big   a value of magnitude 2^-9 or more;
+//   kF16Sub   a nonzero value below 2^-14 (an fp16 subnormal).
+constexpr uint32_t kF16Over = 1u, kF16Big = 2u, kF16Sub = 4u;
+__device__ __forceinline__ uint32_t f16_range_bits(const uint4& a) {
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  uint32_t r = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t m = (w[e] >> (16 * s)) & 0x7FFFu;  // bf16 magnitude bits
+      r |= m >= 0x4780u ? kF16Over : 0u;                // 2^16: next bf16 above 65280
+      r |= m >= 0x3B00u ? kF16Big : 0u;                 // 2^-9
+      r |= (m != 0u && m < 0x3880u) ? kF16Sub : 0u;     // 2^-14
+    }
+  }
+  return r;
+}
+
+// A block of values goes through its fp16 copy when nothing is beyond fp16's range and
+// either some value reaches 2^-9 or none is an fp16 subnormal: every value is then carried
+// to within 2^-16 of the block's largest magnitude (2^-25 <= 2^-16 * 2^-9), as fine as a
+// bf16 hi + lo pair.  Blocks of small values take the bf16 pair instead.
+__device__ __forceinline__ bool f16_block_ok(uint32_t r) {
+  return !(r & kF16Over) && ((r & kF16Big) || !(r & kF16Sub));
+}
+
+// The OR of bits 0-3 of `r` over the wavefront, as wave-uniform bits.
+__device__ __forceinline__ uint32_t wave_or4(uint32_t r) {
+  uint32_t o = 0;
+  if (__ballot(r & 1u)) o |= 1u;
+  if (__ballot(r & 2u)) o |= 2u;
+  if (__ballot(r & 4u)) o |= 4u;
+  if (__ballot(r & 8u)) o |= 8u;
+  return o;
+}
+
 // Workgroup order: the hardware deals consecutive workgroup ids round-robin to the 8
 // XCDs (each with its own L2).  Map them so that each XCD receives a contiguous run of
 // logical tiles (neighbouring query or key blocks of one head share kept tiles).

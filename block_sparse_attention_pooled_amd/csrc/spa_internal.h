@@ -75,6 +75,8 @@ struct BwdArgs {
   uint32_t* bits;   // [BH][ceil(nkb/32)][nqb]
   int32_t* q_idx;   // [BH][nkb][nqb]
   int32_t* q_cnt;   // [BH][nkb]
+  uint16_t* do16;   // [BH][N][d]: fp16 copy of dO (k_dq writes)
+  int32_t* doflag;  // [BH][nqb]: 1 where fp16 cannot carry the block's dO (k_dq writes)
 };
 size_t bwd_workspace_bytes(const Geometry& g);
 void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a);

@@ -135,8 +135,9 @@ SPA_API int spa_sparse_attn_fwd(const spa_dims* dims, const void* q, const void*
 SPA_API size_t spa_fwd_workspace_bytes(const spa_dims* dims);
 
 /* Bytes of device workspace spa_sparse_attn_bwd needs (D = rowsum(dO*O) and lse*log2(e)
- * per row, padded to whole query blocks, the kept-tile
- * bitmap and the per-key-block query-block lists).  0 for rejected dims. */
+ * per row, padded to whole query blocks, the kept-tile bitmap, the per-key-block
+ * query-block lists, an fp16 copy of dO and one int32 flag per query block; 256-byte
+ * aligned sections).  0 for rejected dims. */
 SPA_API size_t spa_bwd_workspace_bytes(const spa_dims* dims);
 
 /*
@@ -146,7 +147,11 @@ SPA_API size_t spa_bwd_workspace_bytes(const spa_dims* dims);
  * the forward pass:  D_t = <dO_t, O_t>;  dS_tu = A_tu (<dO_t, v_u> - D_t);
  * dQ_t = scale * sum_u dS_tu k_u;  dK_u = scale * sum_t dS_tu q_t;  dV_u = sum_t A_tu dO_t.
  * The accumulation order is fixed (ascending block index), so results are bitwise
- * reproducible.  dS enters dQ and dK as a bf16 hi + lo pair.
+ * reproducible.  dS enters dQ and dK as a bf16 hi + lo pair.  In dV = P^T dO, P enters as
+ * one fp16 rounding against an fp16 copy of dO (P <= 1; the copy is exact below 65504 in
+ * magnitude and keeps an absolute 2^-25 below 2^-14); a key block whose query-block list
+ * holds a block of dO beyond fp16's range, or whose V is beyond it, uses bf16 dO with P as
+ * a bf16 hi + lo pair instead.
  *
  *   q, k, v, o, dout  bf16 [B, H, N, d] device (o and lse from spa_sparse_attn_fwd).
  *   o_lo          bf16 [B, H, N, d] device or NULL: the forward pass's residual; with it

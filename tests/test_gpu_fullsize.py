@@ -5,6 +5,7 @@ The mask is compared on every row.  O, LSE and dQ are compared on sampled query 
 (every row of each), dK and dV on sampled key blocks (every query block that keeps them
 contributes), and invariants that hold at any size are checked on the whole tensors.
 """
+import math
 import sys
 
 import numpy as np
@@ -114,7 +115,15 @@ def test_fullsize_gradient_invariants(c2):
         q, k, do = f["q"][0, hh], f["k"][0, hh], f["do"][0, hh]
         # softmax shift invariance: the key gradients of each query row sum to zero
         assert np.abs(dk.sum(axis=0)).max() <= 1e-3 * np.abs(dk).sum(axis=0).max()
-        np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=0.05)
+        # the value gradients sum to the output gradients when each row's P sums to 1.  P
+        # enters dV as one fp16 rounding (relative half-ulp <= 2^-11, variance <= 2^-20 P^2
+        # / 12 per element), so a row's mass is off by eps_t with std <= 2^-10 / sqrt(12)
+        # (sum_u P_tu^2 <= 1), and a column sum by sum_t eps_t dO_t: six standard deviations
+        tol = 6.0 * 2.0 ** -10 / math.sqrt(12.0) * np.sqrt((do ** 2).sum(axis=0))
+        dev = np.abs(dv.sum(axis=0) - do.sum(axis=0))
+        log(f"[fullsize] head {hh}: max column-sum deviation {dev.max():.3e}, "
+            f"max of deviation / tolerance {(dev / tol).max():.3f}")
+        assert np.all(dev <= tol)
         qdq, kdk = float(np.sum(q * dq)), float(np.sum(k * dk))
         assert abs(qdq - kdk) <= 1e-3 * (np.abs(q * dq).sum() + np.abs(k * dk).sum())
 

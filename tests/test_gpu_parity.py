@@ -171,6 +171,107 @@ def test_v_blocks_beyond_fp16_take_the_bf16_path(torch_gpu):
     np.testing.assert_allclose(lse.cpu().numpy(), rl, atol=2e-2)
 
 
+def test_do_and_v_beyond_fp16_take_the_bf16_dv_path(torch_gpu):
+    """In dV = P^T dO the backward reads an fp16 copy of dO with P as one fp16 rounding; a
+    key block whose query-block list holds a block of dO beyond fp16's range (|dO| >= 65504),
+    or whose own V is beyond it, reads bf16 dO with P as a bf16 pair instead.  With dO of
+    one query block and V of one key block scaled past fp16, both forms run in one call: dV
+    is measured against sum_t P_tu |dO_t| (the scale of P's rounding in either form), dQ on
+    the unscaled rows against the usual bound, and dQ, dK elsewhere against their largest
+    reference magnitude."""
+    torch = torch_gpu
+    w = small_workload(1000, 128, 128, grid=(2, 20, 25))
+    g = synth.generate(w)
+    f = {n: synth.bf16_bits_to_f32(g[n]).astype(np.float64) for n in ("q", "k", "v", "do")}
+    big_q = slice(2 * 128, 3 * 128)          # query block 2: dO beyond fp16, every head
+    big_k = slice(5 * 64, 6 * 64)            # key block 5: V beyond fp16, every head
+    f["do"][:, :, big_q, :] *= 2.0 ** 17
+    f["v"][:, :, big_k, :] *= 2.0 ** 17
+    for n in ("v", "do"):
+        g[n] = synth.to_bf16_bits(f[n])
+        f[n] = synth.bf16_bits_to_f32(g[n]).astype(np.float64)
+    q, k, v, do = (to_dev(torch, g[n]) for n in ("q", "k", "v", "do"))
+    kv_idx, kv_cnt = spa.build_mask(q, k, w.blk_q, w.blk_k, w.k_frac, w.p)
+    o, lse, o_lo = spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                                       with_residual=True)
+    dq, dk, dv = spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                                     o_lo=o_lo)
+    torch.cuda.synchronize()
+    idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
+    lists = parity.lists_from_gpu(idx, cnt)
+    nkb = -(-w.N // w.blk_k)
+    for (b, h), rows in lists.items():
+        users = set(rows[2].tolist()) | {5}   # key blocks that take the bf16 form
+        log(f"  head {(b, h)}: {len(users)} of {nkb} key blocks take the bf16 form")
+        assert 1 < len(users) < nkb
+    rq, rk, rv = O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, w.blk_q, w.blk_k)
+    _, _, rabs = O.sparse_attn_bwd(f["q"], f["k"], f["v"], np.abs(f["do"]), lists, w.blk_q,
+                                   w.blk_k)
+    gq, gk, gv = (x.cpu().numpy().astype(np.float64) for x in (dq, dk, dv))
+    for name, x in (("dQ", gq), ("dK", gk), ("dV", gv)):
+        assert np.all(np.isfinite(x)), name
+    err_v = float(np.max(np.abs(gv - rv) / np.maximum(rabs, 1.0)))
+    log(f"  dV: max |error| / sum P|dO| = {err_v:.3e}")
+    assert err_v <= 2.0 ** -11
+    for (b, h), rows in lists.items():  # rows that touch neither scaled block
+        plain = [i for i, r in enumerate(rows) if i != 2 and 5 not in set(r.tolist())]
+        sel = np.concatenate([np.arange(i * w.blk_q, min(w.N, (i + 1) * w.blk_q))
+                              for i in plain])
+        check_close(f"dQ {(b, h)} ({len(plain)} unscaled query blocks)", gq[b, h, sel],
+                    rq[b, h, sel])
+    for name, got, want in (("dQ", gq, rq), ("dK", gk, rk)):
+        rel = float(np.abs(got - want).max() / max(1.0, np.abs(want).max()))
+        log(f"  {name}: max |error| / max |ref| = {rel:.3e}")
+        assert rel <= 1e-3, name
+
+
+def test_small_v_and_do_keep_relative_precision(torch_gpu):
+    """Blocks of small values (all below 2^-9, some below fp16's normal range) do not go
+    through the fp16 copies: head 0 has V scaled by 2^-20 and query block 2 has dO scaled
+    by 2^-20, so the forward's P V and the backward's dV must keep their precision relative
+    to sum_u P_tu |v_u| and sum_t P_tu |dO_t| with no absolute floor (fp16 subnormals would
+    lose most of it).  P itself enters dV in fp16 on blocks that do take the copies, which
+    keeps an absolute 2^-25 below 2^-14: the dV bound adds 2^-24 sum_t |dO_t| over the rows
+    of the query blocks that keep the key, negligible for the scaled block."""
+    torch = torch_gpu
+    w = small_workload(1000, 128, 128, grid=(2, 20, 25))
+    g = synth.generate(w)
+    f = {n: synth.bf16_bits_to_f32(g[n]).astype(np.float64) for n in ("q", "k", "v", "do")}
+    f["v"][:, 0] *= 2.0 ** -20
+    f["do"][:, :, 2 * 128:3 * 128, :] *= 2.0 ** -20
+    for n in ("v", "do"):
+        g[n] = synth.to_bf16_bits(f[n])
+        f[n] = synth.bf16_bits_to_f32(g[n]).astype(np.float64)
+    q, k, v, do = (to_dev(torch, g[n]) for n in ("q", "k", "v", "do"))
+    kv_idx, kv_cnt = spa.build_mask(q, k, w.blk_q, w.blk_k, w.k_frac, w.p)
+    o, lse, o_lo = spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                                       with_residual=True)
+    dq, dk, dv = spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                                     o_lo=o_lo)
+    torch.cuda.synchronize()
+    lists = parity.lists_from_gpu(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy())
+    ro, _ = O.sparse_attn_fwd(f["q"], f["k"], f["v"], lists, w.blk_q, w.blk_k)
+    rabs, _ = O.sparse_attn_fwd(f["q"], f["k"], np.abs(f["v"]), lists, w.blk_q, w.blk_k)
+    full = o.float().cpu().numpy().astype(np.float64) + o_lo.float().cpu().numpy()
+    err_o = float(np.max(np.abs(full - ro) / rabs))
+    log(f"  O + o_lo: max |error| / sum P|v| = {err_o:.3e}")
+    assert err_o <= 2.0 ** -11
+    _, _, rv = O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, w.blk_q, w.blk_k)
+    _, _, rvabs = O.sparse_attn_bwd(f["q"], f["k"], f["v"], np.abs(f["do"]), lists, w.blk_q,
+                                    w.blk_k)
+    gv = dv.cpu().numpy().astype(np.float64)
+    floor = np.zeros_like(gv)  # sum_t |dO_t| over the rows of query blocks keeping the key
+    for (b, h), rows in lists.items():
+        for i, keep in enumerate(rows):
+            s_i = np.abs(f["do"][b, h, i * w.blk_q:(i + 1) * w.blk_q]).sum(axis=0)
+            for j in keep.tolist():
+                floor[b, h, j * w.blk_k:(j + 1) * w.blk_k] += s_i
+    bound = 2.0 ** -11 * rvabs + 2.0 ** -24 * floor
+    err_v = float(np.max(np.abs(gv - rv) / np.maximum(bound, 1e-300)))
+    log(f"  dV: max |error| / (2^-11 sum P|dO| + 2^-24 sum|dO|) = {err_v:.3e}")
+    assert err_v <= 1.0
+
+
 def test_determinism(torch_gpu):
     torch = torch_gpu
     w = small_workload(1000, 128, 128, grid=(2, 20, 25), B=2, H=3)
