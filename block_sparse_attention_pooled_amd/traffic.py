@@ -6,7 +6,8 @@ calibrated against a plain device-to-device copy of known size recorded in the s
 the kernel sources it was measured with: once those sources change, the figure is stale
 and ``load`` returns None.
 
-Also summarises an executed-MFMA counter pass (``summarize-mfma``).
+Also summarises an executed-MFMA counter pass (``summarize-mfma``) and a kernel trace
+(``summarize-trace``).
 
 Command line (writes the markdown summary to stdout):
 
@@ -119,9 +120,41 @@ def load(stage: str, workload: str):
     return None
 
 
+def summarize_trace(trace_csv, title, command) -> str:
+    """Per-kernel call count, total and average duration from a rocprofv3 kernel-trace CSV
+    (``--kernel-trace``), with each kernel's launch shape."""
+    durs = defaultdict(list)
+    shape = {}
+    with open(trace_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+            durs[name].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            if name not in shape:
+                g = lambda k: r.get(k, "?")
+                shape[name] = (f"({g('Grid_Size_X')}, {g('Grid_Size_Y')})", g("Workgroup_Size_X"),
+                               r.get("Arch_VGPR_Count", r.get("VGPR_Count", "?")),
+                               g("Accum_VGPR_Count"),
+                               r.get("LDS_Block_Size", r.get("Group_Segment_Size", "?")))
+    total = sum(sum(v) for v in durs.values())
+    out = [f"# Kernel trace: {title}", "", "Command (from the repository root on one MI355X):",
+           "", "```", command, "```", "",
+           "| kernel | calls | total (us) | average (us) | share |", "|---|---|---|---|---|"]
+    order = sorted(durs, key=lambda n: -sum(durs[n]))
+    for n in order:
+        t = sum(durs[n])
+        out.append(f"| `{n}` | {len(durs[n])} | {t:.1f} | {t / len(durs[n]):.1f} | "
+                   f"{100.0 * t / total:.1f} % |")
+    out += ["", "Launch shapes:", "",
+            "| kernel | grid (x, y) | workgroup | arch VGPR | acc VGPR | LDS bytes |",
+            "|---|---|---|---|---|---|"]
+    for n in order:
+        out.append(f"| `{n}` | " + " | ".join(shape[n]) + " |")
+    return "\n".join(out) + "\n"
+
+
 def summarize_mfma(csv_path, workload, command) -> str:
     """Executed MFMA work per dispatch from SQ_INSTS_MFMA (every MFMA here is a
-    32x32x16 bf16 instruction: 32768 FLOP per wavefront instruction) over the dispatch's
+    32x32x16 bf16 or fp16 instruction: 32768 FLOP per wavefront instruction) over the dispatch's
     duration, with the MFMA-busy and GPU-busy cycle counters as recorded."""
     per = defaultdict(lambda: defaultdict(list))
     dur = defaultdict(dict)
@@ -133,7 +166,8 @@ def summarize_mfma(csv_path, workload, command) -> str:
     out = [f"# Executed MFMA work per launch: {workload}", "",
            "Counter pass (from the repository root on one MI355X):", "", "```", command, "```",
            "",
-           "Executed FLOP = SQ_INSTS_MFMA x 32768 (all MFMAs are v_mfma_f32_32x32x16_bf16); "
+           "Executed FLOP = SQ_INSTS_MFMA x 32768 (all MFMAs are v_mfma_f32_32x32x16_bf16 or "
+           "_f16); "
            "the rate divides by the dispatch's own duration in this run.  Credited (kept-tile "
            "algorithmic) FLOP are lower: the precision splits and the recomputation in the "
            "backward are executed but not credited.", "",
@@ -164,6 +198,10 @@ def main(argv=None):
     s.add_argument("--workload", required=True)
     s.add_argument("--command-fetch", required=True)
     s.add_argument("--command-write", required=True)
+    t = sub.add_parser("summarize-trace")
+    t.add_argument("--trace", required=True)
+    t.add_argument("--title", required=True)
+    t.add_argument("--command", required=True)
     m = sub.add_parser("summarize-mfma")
     m.add_argument("--csv", required=True)
     m.add_argument("--workload", required=True)
@@ -172,6 +210,8 @@ def main(argv=None):
     if a.cmd == "summarize":
         sys.stdout.write(summarize(a.fetch, a.write, a.copy_mib, a.workload, a.command_fetch,
                                    a.command_write))
+    elif a.cmd == "summarize-trace":
+        sys.stdout.write(summarize_trace(a.trace, a.title, a.command))
     else:
         sys.stdout.write(summarize_mfma(a.csv, a.workload, a.command))
 
