@@ -228,14 +228,5 @@ __device__ __forceinline__ uint32_t wave_or4(uint32_t r) {
   return o;
 }
 
-// Workgroup order: the hardware deals consecutive workgroup ids round-robin to the 8
-// XCDs (each with its own L2).  Map them so that each XCD receives a contiguous run of
-// logical tiles (neighbouring query or key blocks of one head share kept tiles).
-__device__ __forceinline__ int xcd_remap(int id, int total) {
-  constexpr int X = 8;
-  const int whole = total - total % X;
-  if (id >= whole) return id;
-  return (id % X) * (whole / X) + id / X;
-}
 
 }  // namespace spa

@@ -4,9 +4,11 @@
 //
 // k_pool    streams Q and K once from HBM (16-byte loads) and writes the block means in
 //           fp64.  Sums of bf16 values are exact in fp64, so the means are the correctly
-//           rounded means.
-// k_select  one workgroup per (b, h, 8 query blocks): the pooled logits of its 8 rows
-//           (fp64 FMA against the transposed pooled K), then one wavefront per row:
+//           rounded means.  Workgroups run in XCD-contiguous order, so that the 8-byte
+//           writes of neighbouring key blocks into one line of the transposed pooled K
+//           meet in one L2.
+// k_select  one workgroup per (b, h, 8 query blocks), XCD-contiguous: the pooled logits of
+//           its 8 rows (fp64 FMA against the transposed pooled K), then one wavefront per row:
 //           fp64 softmax, and a most-significant-digit radix select over the fp64 bit
 //           patterns of the probabilities that finds the last element of the kept prefix.
 //           The prefix condition "count >= Lk and cumulative probability >= p" is checked
@@ -29,10 +31,13 @@ __global__ __launch_bounds__(256) void k_pool(const uint16_t* __restrict__ q,
   constexpr int C = D / 8;    // 16-byte chunks per row
   constexpr int R = 256 / C;  // rows per pass
   __shared__ double part[R][D];
-  const int bh = blockIdx.y;
-  const bool is_q = (int)blockIdx.x < nqb;
+  const int per_head = nqb + nkb;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / per_head;
+  const int x = tile - bh * per_head;
+  const bool is_q = x < nqb;
   const int blk = is_q ? blk_q : kBlkK;
-  const int b = is_q ? blockIdx.x : blockIdx.x - nqb;
+  const int b = is_q ? x : x - nqb;
   const int row0 = b * blk;
   const int nrows = min(blk, N - row0);
   const uint16_t* src = (is_q ? q : k) + ((size_t)bh * N + row0) * D;
@@ -257,8 +262,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
       reinterpret_cast<unsigned long long*>(srow + (size_t)kSelRows * nkb);  // [8][256]
   uint32_t* hcnt = reinterpret_cast<uint32_t*>(hmass + kSelRows * 256);      // [8][256]
 
-  const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * kSelRows;
+  // workgroups in XCD-contiguous order: the 8 query-block groups of one head read the
+  // same pooled K, which then stays in that XCD's L2
+  const int ngroups = (nqb + kSelRows - 1) / kSelRows;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / ngroups;
+  const int i0 = (tile - bh * ngroups) * kSelRows;
   const int t = threadIdx.x;
   for (int x = t; x < kSelRows * D; x += kSelThreads) {
     const int g = x / D, c = x % D;
@@ -396,7 +405,7 @@ static hipError_t launch_select_t(const MaskArgs& a, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
   }
-  dim3 grid((g.nqb + kSelRows - 1) / kSelRows, (unsigned)g.bh());
+  dim3 grid((unsigned)(((g.nqb + kSelRows - 1) / kSelRows) * g.bh()));
   hipLaunchKernelGGL((k_select<D, E>), grid, dim3(kSelThreads), shm, s, a.qbar, a.kbar_t, g.nqb,
                      g.nkb, a.pooled_scale, a.lk, a.p_all, a.wp, a.kv_idx, a.kv_cnt, a.rule_len);
   return hipGetLastError();
@@ -406,7 +415,7 @@ template <int D>
 static hipError_t launch_mask_d(const MaskArgs& a, unsigned stages, hipStream_t s) {
   const Geometry& g = a.g;
   if (stages & 1u) {
-    dim3 grid(g.nqb + g.nkb, (unsigned)g.bh());
+    dim3 grid((unsigned)((g.nqb + g.nkb) * g.bh()));
     hipLaunchKernelGGL((k_pool<D>), grid, dim3(256), 0, s, a.q, a.k, g.N, g.blk_q, g.nqb, g.nkb,
                        a.qbar, a.kbar_t);
     hipError_t e = hipGetLastError();

@@ -76,4 +76,14 @@ __device__ __forceinline__ float swap_halves(float x) {  // value of lane l ^ 32
   return __shfl_xor(x, 32, 64);
 }
 
+// Workgroup order: the hardware deals consecutive workgroup ids round-robin to the 8
+// XCDs (each with its own L2).  Map them so that each XCD receives a contiguous run of
+// logical tiles (neighbouring query or key blocks of one head share kept tiles).
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  constexpr int X = 8;
+  const int whole = total - total % X;
+  if (id >= whole) return id;
+  return (id % X) * (whole / X) + id / X;
+}
+
 }  // namespace spa
