@@ -6,6 +6,8 @@
 // Launch sequence (one stream):
 //   k_bitmap    the kept-tile bitmap, transposed: word w of query block i at [w][i];
 //   k_collists  per key block j, the ascending list of query blocks that keep j;
+//   k_order     the dispatch order of the dK/dV workgroups (longest lists first within
+//               each XCD's share);
 //   k_dq        one workgroup per (b, h, query block): first D_t = <dO_t, O_t> in fp32
 //               (O = o + o_lo when the forward pass supplied its rounding residual) and
 //               lse_t * log2(e) for its rows, kept in registers and written out for the
@@ -73,6 +75,56 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
       base += __popcll(ball);
     }
     if (lane == 0) q_cnt[(size_t)bh * nkb + j] = base;
+  }
+}
+
+// Dispatch order of the dK/dV workgroups: within each XCD's contiguous share of the key
+// blocks (xcd_remap), the longest query-block lists first, so that the workgroups that
+// start last are short ones and the XCDs finish together.  One workgroup per share (a
+// counting sort on list length); the order among equal lengths is left to LDS atomics,
+// which affects only scheduling, never results.
+__global__ __launch_bounds__(1024) void k_order(const int32_t* __restrict__ q_cnt, int total,
+                                                int nqb, int32_t* __restrict__ order) {
+  extern __shared__ int32_t hist[];  // [nqb + 1]: counts by bin, then the bins' offsets
+  __shared__ int32_t wsum[16];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int whole = total - total % 8, per = whole / 8, base = (int)blockIdx.x * per;
+  const int nb = nqb + 1;
+  for (int r = t; r < nb; r += 1024) hist[r] = 0;
+  if (blockIdx.x == 0)
+    for (int x = whole + t; x < total; x += 1024) order[x] = x;  // the few left over
+  __syncthreads();
+  // bin nqb - len: ascending bins are descending lengths
+  for (int x = t; x < per; x += 1024) atomicAdd(&hist[nqb - min(max(q_cnt[base + x], 0), nqb)], 1);
+  __syncthreads();
+  const int B = (nb + 1023) / 1024;  // bins per thread, contiguous
+  int local = 0;
+  for (int u = 0; u < B; ++u) {
+    const int r = t * B + u;
+    if (r < nb) local += hist[r];
+  }
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int x = 0; x < wv; ++x) run += wsum[x];
+  for (int u = 0; u < B; ++u) {  // own bins only: no other thread touches them here
+    const int r = t * B + u;
+    if (r < nb) {
+      const int h = hist[r];
+      hist[r] = run;
+      run += h;
+    }
+  }
+  __syncthreads();
+  for (int x = t; x < per; x += 1024) {
+    const int pos = atomicAdd(&hist[nqb - min(max(q_cnt[base + x], 0), nqb)], 1);
+    order[base + pos] = base + x;
   }
 }
 
@@ -270,7 +322,7 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
     const int32_t* __restrict__ q_idx, const int32_t* __restrict__ q_cnt, int N, int npad,
     int nqb, int nkb, int total, float scale_log2, float scale, void* __restrict__ dk_out,
     void* __restrict__ dv_out, int grad_bf16, const uint16_t* __restrict__ do16,
-    const int32_t* __restrict__ doflag) {
+    const int32_t* __restrict__ doflag, const int32_t* __restrict__ order) {
   constexpr int DB = D / 32;
   constexpr int KS = D / 16;
   constexpr int HR = 64;                 // query rows per stage
@@ -285,7 +337,7 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   __shared__ uint32_t wbits[8];  // per wavefront: fp16 range classes of V, listed dO flags
   static_assert(2 * DB * 16 * 64 * 4 <= SLOT * 2, "reduction buffer reuses a slot");
 
-  const int tile_id = xcd_remap(blockIdx.x, total);
+  const int tile_id = order[xcd_remap(blockIdx.x, total)];
   const int bh = tile_id / nkb;
   const int j = tile_id - bh * nkb;
   const int lane = threadIdx.x & 63;
@@ -670,7 +722,8 @@ size_t bwd_workspace_bytes(const Geometry& g) {
          align_up(bh * g.nkb * g.nqb * sizeof(int32_t), 256) +
          align_up(bh * g.nkb * sizeof(int32_t), 256) +
          align_up(bh * (size_t)g.N * g.d * sizeof(uint16_t), 256) +
-         align_up(bh * g.nqb * sizeof(int32_t), 256);
+         align_up(bh * g.nqb * sizeof(int32_t), 256) +
+         align_up(bh * g.nkb * sizeof(int32_t), 256);
 }
 
 void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a) {
@@ -689,6 +742,8 @@ void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a) {
   a->do16 = reinterpret_cast<uint16_t*>(p);
   p += align_up(bh * (size_t)g.N * g.d * sizeof(uint16_t), 256);
   a->doflag = reinterpret_cast<int32_t*>(p);
+  p += align_up(bh * g.nqb * sizeof(int32_t), 256);
+  a->order = reinterpret_cast<int32_t*>(p);
 }
 
 template <int D, int BQ>
@@ -702,6 +757,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
                        a.kv_cnt, g.nqb, g.nkb, nw, a.bits);
     hipLaunchKernelGGL(k_collists, dim3(nw, (unsigned)g.bh()), dim3(256),
                        g.nqb * sizeof(uint32_t), s, a.bits, g.nqb, g.nkb, nw, a.q_idx, a.q_cnt);
+    hipLaunchKernelGGL(k_order, dim3(8), dim3(1024), (g.nqb + 1) * sizeof(int32_t), s, a.q_cnt,
+                       (int)(g.nkb * g.bh()), g.nqb, a.order);
   }
   if (stages & 2u) {
     const int total = (int)(g.nqb * g.bh());
@@ -714,7 +771,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
     const int total = (int)(g.nkb * g.bh());
     hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(total), dim3(512), 0, s, a.q, a.k, a.v, a.dout,
                        a.lse2, a.dsum, a.q_idx, a.q_cnt, g.N, npad, g.nqb, g.nkb, total, sl2,
-                       a.scale, a.dk, a.dv, a.grad_bf16, a.do16, a.doflag);
+                       a.scale, a.dk, a.dv, a.grad_bf16, a.do16, a.doflag, a.order);
   }
   return hipGetLastError();
 }

@@ -76,11 +76,13 @@ struct BwdArgs {
   int32_t* q_idx;   // [BH][nkb][nqb]
   int32_t* q_cnt;   // [BH][nkb]
   uint16_t* do16;   // [BH][N][d]: fp16 copy of dO (k_dq writes)
-  int32_t* doflag;  // [BH][nqb]: 1 where fp16 cannot carry the block's dO (k_dq writes)
+  int32_t* doflag;  // [BH][nqb]: 1 where the block is not read through do16 (k_dq writes)
+  int32_t* order;   // [BH * nkb]: dK/dV workgroup dispatch order (k_order writes)
 };
 size_t bwd_workspace_bytes(const Geometry& g);
 void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a);
-// stage bits: 1 = D and the column lists, 2 = dK/dV, 4 = dQ
+// stage bits: 1 = the column lists and the dK/dV order, 2 = dQ (also D, lse2 and the fp16
+// copy of dO), 4 = dK/dV
 hipError_t launch_bwd(const BwdArgs& a, unsigned stages, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -136,8 +136,8 @@ SPA_API size_t spa_fwd_workspace_bytes(const spa_dims* dims);
 
 /* Bytes of device workspace spa_sparse_attn_bwd needs (D = rowsum(dO*O) and lse*log2(e)
  * per row, padded to whole query blocks, the kept-tile bitmap, the per-key-block
- * query-block lists, an fp16 copy of dO and one int32 flag per query block; 256-byte
- * aligned sections).  0 for rejected dims. */
+ * query-block lists and their dispatch order, an fp16 copy of dO and one int32 flag per
+ * query block; 256-byte aligned sections).  0 for rejected dims. */
 SPA_API size_t spa_bwd_workspace_bytes(const spa_dims* dims);
 
 /*
@@ -175,9 +175,9 @@ SPA_API int spa_sparse_attn_bwd(const spa_dims* dims, const void* q, const void*
  * call).  Stage bits of spa_build_mask_stages: SPA_MASK_POOL (block means of Q and K
  * into the workspace), SPA_MASK_SELECT (pooled softmax and selection from the
  * workspace).  Stage bits of spa_sparse_attn_bwd_stages: SPA_BWD_PREP (the
- * per-key-block query-block lists into the workspace), SPA_BWD_DQ (dQ; also writes D and
- * lse * log2(e) of every row into the workspace), SPA_BWD_DKDV (dK, dV; reads what
- * SPA_BWD_DQ wrote).  A zero or unknown stage mask gives SPA_E_PARAM.
+ * per-key-block query-block lists and the order in which their workgroups run, into the
+ * workspace), SPA_BWD_DQ (dQ; also writes D and lse * log2(e) of every row and the fp16
+ * copy of dO into the workspace), SPA_BWD_DKDV (dK, dV; reads what the other two wrote).  A zero or unknown stage mask gives SPA_E_PARAM.
  */
 enum {
   SPA_MASK_POOL = 1, SPA_MASK_SELECT = 2, SPA_MASK_ALL = 3,
