@@ -7,7 +7,7 @@
 //   k_bitmap    the kept-tile bitmap, transposed: word w of query block i at [w][i];
 //   k_collists  per key block j, the ascending list of query blocks that keep j;
 //   k_order     the dispatch order of the dK/dV workgroups (longest lists first within
-//               each XCD's share);
+//               each window of 32 neighbouring key blocks of an XCD's share);
 //   k_dq        one workgroup per (b, h, query block): first D_t = <dO_t, O_t> in fp32
 //               (O = o + o_lo when the forward pass supplied its rounding residual) and
 //               lse_t * log2(e) for its rows, kept in registers and written out for the
@@ -78,54 +78,37 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
   }
 }
 
-// Dispatch order of the dK/dV workgroups: within each XCD's contiguous share of the key
-// blocks (xcd_remap), the longest query-block lists first, so that the workgroups that
-// start last are short ones and the XCDs finish together.  One workgroup per share (a
-// counting sort on list length); the order among equal lengths is left to LDS atomics,
-// which affects only scheduling, never results.
-__global__ __launch_bounds__(1024) void k_order(const int32_t* __restrict__ q_cnt, int total,
-                                                int nqb, int32_t* __restrict__ order) {
-  extern __shared__ int32_t hist[];  // [nqb + 1]: counts by bin, then the bins' offsets
-  __shared__ int32_t wsum[16];
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int whole = total - total % 8, per = whole / 8, base = (int)blockIdx.x * per;
-  const int nb = nqb + 1;
-  for (int r = t; r < nb; r += 1024) hist[r] = 0;
-  if (blockIdx.x == 0)
-    for (int x = whole + t; x < total; x += 1024) order[x] = x;  // the few left over
-  __syncthreads();
-  // bin nqb - len: ascending bins are descending lengths
-  for (int x = t; x < per; x += 1024) atomicAdd(&hist[nqb - min(max(q_cnt[base + x], 0), nqb)], 1);
-  __syncthreads();
-  const int B = (nb + 1023) / 1024;  // bins per thread, contiguous
-  int local = 0;
-  for (int u = 0; u < B; ++u) {
-    const int r = t * B + u;
-    if (r < nb) local += hist[r];
+// Dispatch order of the dK/dV workgroups.  Each XCD runs a contiguous share of the key
+// blocks (xcd_remap), 32 at a time on its 32 CUs; within every window of 32 consecutive
+// key blocks of a share, the longest query-block lists go first, so that the workgroups
+// that start last are short ones and the XCDs finish together, while the key blocks that
+// run side by side stay neighbours (they read the same Q and dO tiles from L2).  One
+// thread per key block ranks its list length within its window (ties by position), so
+// the order is deterministic; it affects only scheduling, never results.
+constexpr int kOrderWindow = 32;
+
+// One workgroup per 256 consecutive key blocks of a share (eight windows), plus one for
+// the key blocks left over after the eight equal shares, which run in place.
+__global__ __launch_bounds__(256) void k_order(const int32_t* __restrict__ q_cnt, int total,
+                                               int32_t* __restrict__ order) {
+  __shared__ int32_t lens[256];
+  const int whole = total - total % 8, per = whole / 8;
+  const int wpb = (per + 255) / 256;  // workgroups per share
+  const int t = threadIdx.x;
+  if ((int)blockIdx.x == 8 * wpb) {
+    for (int x = whole + t; x < total; x += 256) order[x] = x;
+    return;
   }
-  int incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) wsum[wv] = incl;
+  const int share = blockIdx.x / wpb, wb = blockIdx.x - share * wpb;
+  const int b0 = share * per + wb * 256, n = min(256, (share + 1) * per - b0);
+  if (t < n) lens[t] = q_cnt[b0 + t];
   __syncthreads();
-  int run = incl - local;
-  for (int x = 0; x < wv; ++x) run += wsum[x];
-  for (int u = 0; u < B; ++u) {  // own bins only: no other thread touches them here
-    const int r = t * B + u;
-    if (r < nb) {
-      const int h = hist[r];
-      hist[r] = run;
-      run += h;
-    }
-  }
-  __syncthreads();
-  for (int x = t; x < per; x += 1024) {
-    const int pos = atomicAdd(&hist[nqb - min(max(q_cnt[base + x], 0), nqb)], 1);
-    order[base + pos] = base + x;
-  }
+  if (t >= n) return;
+  const int w0 = t / kOrderWindow * kOrderWindow, w1 = min(w0 + kOrderWindow, n);
+  const int len = lens[t];
+  int rank = 0;
+  for (int y = w0; y < w1; ++y) rank += (lens[y] > len || (lens[y] == len && y < t)) ? 1 : 0;
+  order[b0 + w0 + rank] = b0 + t;
 }
 
 // ------------------------------------------------------------------------------------
@@ -757,8 +740,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
                        a.kv_cnt, g.nqb, g.nkb, nw, a.bits);
     hipLaunchKernelGGL(k_collists, dim3(nw, (unsigned)g.bh()), dim3(256),
                        g.nqb * sizeof(uint32_t), s, a.bits, g.nqb, g.nkb, nw, a.q_idx, a.q_cnt);
-    hipLaunchKernelGGL(k_order, dim3(8), dim3(1024), (g.nqb + 1) * sizeof(int32_t), s, a.q_cnt,
-                       (int)(g.nkb * g.bh()), g.nqb, a.order);
+    const int nk = (int)(g.nkb * g.bh()), per = (nk - nk % 8) / 8;
+    hipLaunchKernelGGL(k_order, dim3(8 * ((per + 255) / 256) + 1), dim3(256), 0, s, a.q_cnt, nk,
+                       a.order);
   }
   if (stages & 2u) {
     const int total = (int)(g.nqb * g.bh());

@@ -6,8 +6,8 @@ calibrated against a plain device-to-device copy of known size recorded in the s
 the kernel sources it was measured with: once those sources change, the figure is stale
 and ``load`` returns None.
 
-Also summarises an executed-MFMA counter pass (``summarize-mfma``) and a kernel trace
-(``summarize-trace``).
+Also summarises an executed-MFMA counter pass (``summarize-mfma``), a kernel trace
+(``summarize-trace``) and a breakdown of SIMD cycles (``summarize-stalls``).
 
 Command line (writes the markdown summary to stdout):
 
@@ -152,6 +152,64 @@ def summarize_trace(trace_csv, title, command) -> str:
     return "\n".join(out) + "\n"
 
 
+STALL_KERNELS = ("spa::k_dkdv", "spa::k_dq", "spa::k_fwd", "spa::k_select", "spa::k_pool")
+
+
+def _counters(path):
+    per = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(dict)
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+            per[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[name][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    avg = {n: {k: sum(v) / len(v) for k, v in c.items()} for n, c in per.items()}
+    d_us = {n: sum(v.values()) / len(v) / 1e3 for n, v in dur.items()}
+    return avg, d_us
+
+
+def summarize_stalls(csv_a, csv_b, workload, cmd_a, cmd_b, simds=1024, xcds=8) -> str:
+    """Where the SIMDs' cycles go, per kernel, from two counter passes: MFMA-pipe busy
+    cycles, VALU issue (4 cycles per non-MFMA VALU instruction of a 64-wide wavefront),
+    their overlap, and the wavefront states.  The clock is GRBM_GUI_ACTIVE over the
+    dispatch (summed over the XCDs); SIMD cycles = SIMDs x duration x clock."""
+    a, da = _counters(csv_a)
+    b, db = _counters(csv_b)
+    out = [f"# Where the SIMD cycles go: {workload}", "",
+           "Counter passes (from the repository root on one MI355X):", "", "```", cmd_a,
+           cmd_b, "```", "",
+           "Per kernel, as fractions of SIMD cycles (1024 SIMDs x duration x the clock from "
+           "GRBM_GUI_ACTIVE): MFMA = SQ_VALU_MFMA_BUSY_CYCLES; VALU = 4 x (SQ_INSTS_VALU - "
+           "SQ_INSTS_MFMA), the issue cycles of the other vector instructions; both = "
+           "SQ_VALU_MFMA_COEXEC_CYCLES.  Wavefront states are fractions of SQ_WAVE_CYCLES.", "",
+           "| kernel | us | GHz | MFMA only | VALU only | both | neither | waiting (SQ_WAIT_ANY) "
+           "| ready, not issued (SQ_WAIT_INST_ANY) | issuing (SQ_ACTIVE_INST_ANY) | "
+           "exp / transcendental instr | LDS instr |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for pre in STALL_KERNELS:
+        na = max((n for n in a if n.startswith(pre)), key=lambda n: da[n], default=None)
+        nb = max((n for n in b if n.startswith(pre)), key=lambda n: db[n], default=None)
+        if na is None or nb is None:
+            continue
+        ca, cb = a[na], b[nb]
+        clk = ca.get("GRBM_GUI_ACTIVE", 0.0) / xcds / (da[na] * 1e-6)
+        cyc = simds * da[na] * 1e-6 * clk
+        if cyc <= 0:
+            continue
+        mf = ca.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / cyc
+        va = 4.0 * (cb.get("SQ_INSTS_VALU", 0.0) - cb.get("SQ_INSTS_MFMA", 0.0)) / cyc
+        bo = ca.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / cyc
+        wc = ca.get("SQ_WAVE_CYCLES", 0.0) or float("nan")
+        out.append(
+            f"| `{na}` | {da[na]:.0f} | {clk / 1e9:.2f} | {100 * (mf - bo):.0f} % | "
+            f"{100 * (va - bo):.0f} % | {100 * bo:.0f} % | {100 * (1 - mf - va + bo):.0f} % | "
+            f"{100 * ca.get('SQ_WAIT_ANY', 0) / wc:.0f} % | "
+            f"{100 * ca.get('SQ_WAIT_INST_ANY', 0) / wc:.0f} % | "
+            f"{100 * ca.get('SQ_ACTIVE_INST_ANY', 0) / wc:.0f} % | "
+            f"{cb.get('SQ_INSTS_VALU_TRANS_F32', 0):.3g} | {cb.get('SQ_INSTS_LDS', 0):.3g} |")
+    return "\n".join(out) + "\n"
+
+
 def summarize_mfma(csv_path, workload, command) -> str:
     """Executed MFMA work per dispatch from SQ_INSTS_MFMA (every MFMA here is a
     32x32x16 bf16 or fp16 instruction: 32768 FLOP per wavefront instruction) over the dispatch's
@@ -202,6 +260,12 @@ def main(argv=None):
     t.add_argument("--trace", required=True)
     t.add_argument("--title", required=True)
     t.add_argument("--command", required=True)
+    st = sub.add_parser("summarize-stalls")
+    st.add_argument("--csv-a", required=True)
+    st.add_argument("--csv-b", required=True)
+    st.add_argument("--workload", required=True)
+    st.add_argument("--command-a", required=True)
+    st.add_argument("--command-b", required=True)
     m = sub.add_parser("summarize-mfma")
     m.add_argument("--csv", required=True)
     m.add_argument("--workload", required=True)
@@ -210,6 +274,9 @@ def main(argv=None):
     if a.cmd == "summarize":
         sys.stdout.write(summarize(a.fetch, a.write, a.copy_mib, a.workload, a.command_fetch,
                                    a.command_write))
+    elif a.cmd == "summarize-stalls":
+        sys.stdout.write(summarize_stalls(a.csv_a, a.csv_b, a.workload, a.command_a,
+                                          a.command_b))
     elif a.cmd == "summarize-trace":
         sys.stdout.write(summarize_trace(a.trace, a.title, a.command))
     else:
