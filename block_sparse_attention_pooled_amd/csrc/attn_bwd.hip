@@ -5,9 +5,9 @@
 //
 // Launch sequence (one stream):
 //   k_bitmap    the kept-tile bitmap, transposed: word w of query block i at [w][i];
-//   k_collists  per key block j, the ascending list of query blocks that keep j;
-//   k_order     the dispatch order of the dK/dV workgroups (longest lists first within
-//               each window of 32 neighbouring key blocks of an XCD's share);
+//   k_collists  per key block j, the ascending list of query blocks that keep j, and the
+//               dispatch order of the dK/dV workgroups (longest lists first within each
+//               run of 32 neighbouring key blocks);
 //   k_dq        one workgroup per (b, h, query block): first D_t = <dO_t, O_t> in fp32
 //               (O = o + o_lo when the forward pass supplied its rounding residual) and
 //               lse_t * log2(e) for its rows, kept in registers and written out for the
@@ -51,10 +51,18 @@ __global__ __launch_bounds__(64) void k_bitmap(const int32_t* __restrict__ kv_id
   if (t < nw) bits[((size_t)bh * nw + t) * nqb + i] = words[t];
 }
 
+// Column lists, 32 key blocks of one head per workgroup, and the dispatch order of their
+// dK/dV workgroups: within these 32 neighbouring key blocks the longest lists go first
+// (ranked by length, ties by position, so the order is deterministic).  The workgroups
+// that start last on an XCD are then short ones, while the key blocks that run side by
+// side stay neighbours that read the same Q and dO tiles from L2.  The order affects only
+// scheduling, never results.
 __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ bits, int nqb,
                                                   int nkb, int nw, int32_t* __restrict__ q_idx,
-                                                  int32_t* __restrict__ q_cnt) {
+                                                  int32_t* __restrict__ q_cnt,
+                                                  int32_t* __restrict__ order) {
   extern __shared__ uint32_t colw[];  // [nqb]
+  __shared__ int32_t lens[32];
   const int bh = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
   const uint32_t* src = bits + ((size_t)bh * nw + w) * nqb;
   for (int x = t; x < nqb; x += 256) colw[x] = src[x];
@@ -74,41 +82,19 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
       if (on) out[base + before] = i;
       base += __popcll(ball);
     }
-    if (lane == 0) q_cnt[(size_t)bh * nkb + j] = base;
+    if (lane == 0) {
+      q_cnt[(size_t)bh * nkb + j] = base;
+      lens[b] = base;
+    }
   }
-}
-
-// Dispatch order of the dK/dV workgroups.  Each XCD runs a contiguous share of the key
-// blocks (xcd_remap), 32 at a time on its 32 CUs; within every window of 32 consecutive
-// key blocks of a share, the longest query-block lists go first, so that the workgroups
-// that start last are short ones and the XCDs finish together, while the key blocks that
-// run side by side stay neighbours (they read the same Q and dO tiles from L2).  One
-// thread per key block ranks its list length within its window (ties by position), so
-// the order is deterministic; it affects only scheduling, never results.
-constexpr int kOrderWindow = 32;
-
-// One workgroup per 256 consecutive key blocks of a share (eight windows), plus one for
-// the key blocks left over after the eight equal shares, which run in place.
-__global__ __launch_bounds__(256) void k_order(const int32_t* __restrict__ q_cnt, int total,
-                                               int32_t* __restrict__ order) {
-  __shared__ int32_t lens[256];
-  const int whole = total - total % 8, per = whole / 8;
-  const int wpb = (per + 255) / 256;  // workgroups per share
-  const int t = threadIdx.x;
-  if ((int)blockIdx.x == 8 * wpb) {
-    for (int x = whole + t; x < total; x += 256) order[x] = x;
-    return;
-  }
-  const int share = blockIdx.x / wpb, wb = blockIdx.x - share * wpb;
-  const int b0 = share * per + wb * 256, n = min(256, (share + 1) * per - b0);
-  if (t < n) lens[t] = q_cnt[b0 + t];
   __syncthreads();
-  if (t >= n) return;
-  const int w0 = t / kOrderWindow * kOrderWindow, w1 = min(w0 + kOrderWindow, n);
-  const int len = lens[t];
-  int rank = 0;
-  for (int y = w0; y < w1; ++y) rank += (lens[y] > len || (lens[y] == len && y < t)) ? 1 : 0;
-  order[b0 + w0 + rank] = b0 + t;
+  const int nb = min(32, nkb - w * 32);
+  if (t < nb) {
+    int rank = 0;
+    for (int y = 0; y < nb; ++y) rank += (lens[y] > lens[t] || (lens[y] == lens[t] && y < t)) ? 1 : 0;
+    const size_t first = (size_t)bh * nkb + w * 32;
+    order[first + rank] = (int32_t)(first + t);
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -739,9 +725,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
     hipLaunchKernelGGL(k_bitmap, dim3(g.nqb, (unsigned)g.bh()), dim3(64), 0, s, a.kv_idx,
                        a.kv_cnt, g.nqb, g.nkb, nw, a.bits);
     hipLaunchKernelGGL(k_collists, dim3(nw, (unsigned)g.bh()), dim3(256),
-                       g.nqb * sizeof(uint32_t), s, a.bits, g.nqb, g.nkb, nw, a.q_idx, a.q_cnt);
-    const int nk = (int)(g.nkb * g.bh()), per = (nk - nk % 8) / 8;
-    hipLaunchKernelGGL(k_order, dim3(8 * ((per + 255) / 256) + 1), dim3(256), 0, s, a.q_cnt, nk,
+                       g.nqb * sizeof(uint32_t), s, a.bits, g.nqb, g.nkb, nw, a.q_idx, a.q_cnt,
                        a.order);
   }
   if (stages & 2u) {
