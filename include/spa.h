@@ -118,9 +118,11 @@ SPA_API int spa_build_mask(const spa_dims* dims, const void* q, const void* k, d
  *                 2^-9 |dO| |O|.  With o_lo the probabilities enter P*V as one fp16
  *                 rounding against an fp16 copy of V (fp16 has three more mantissa bits
  *                 than bf16), so o + o_lo carries O to about 12 significant bits.  A query
- *                 block whose list holds a key block of V with a value of magnitude 65504
- *                 or more (beyond fp16) takes bf16 V with P as a bf16 hi + lo pair
- *                 instead (about 16 bits).  Without o_lo, P enters as bf16.
+ *                 block whose list holds a key block of V that the copy does not carry
+ *                 to within 2^-16 of the block's largest magnitude (a value of magnitude
+ *                 65504 or more, or only values below 2^-9 with some in fp16's subnormal
+ *                 range) takes bf16 V with P as a bf16 hi + lo pair instead (about 16
+ *                 bits).  Without o_lo, P enters as bf16.
  *   lse           fp32 [B, H, N] device, out (natural log).
  *   ws, ws_bytes  device workspace of at least spa_fwd_workspace_bytes(dims) when o_lo is
  *                 given (the fp16 copy of V and a flag per key block); ignored, and may be
@@ -148,10 +150,12 @@ SPA_API size_t spa_bwd_workspace_bytes(const spa_dims* dims);
  * dQ_t = scale * sum_u dS_tu k_u;  dK_u = scale * sum_t dS_tu q_t;  dV_u = sum_t A_tu dO_t.
  * The accumulation order is fixed (ascending block index), so results are bitwise
  * reproducible.  dS enters dQ and dK as a bf16 hi + lo pair.  In dV = P^T dO, P enters as
- * one fp16 rounding against an fp16 copy of dO (P <= 1; the copy is exact below 65504 in
- * magnitude and keeps an absolute 2^-25 below 2^-14); a key block whose query-block list
- * holds a block of dO beyond fp16's range, or whose V is beyond it, uses bf16 dO with P as
- * a bf16 hi + lo pair instead.
+ * one fp16 rounding against an fp16 copy of dO (P <= 1; the copy is exact from 2^-14 to
+ * below 65504 in magnitude and keeps an absolute 2^-25 below 2^-14).  A key block whose
+ * query-block list holds a query block of dO, or whose own V, that the copy does not
+ * carry to within 2^-16 of the block's largest magnitude (a value beyond fp16's range, or
+ * only values below 2^-9 with some in fp16's subnormal range) uses bf16 dO with P as a
+ * bf16 hi + lo pair instead.
  *
  *   q, k, v, o, dout  bf16 [B, H, N, d] device (o and lse from spa_sparse_attn_fwd).
  *   o_lo          bf16 [B, H, N, d] device or NULL: the forward pass's residual; with it
