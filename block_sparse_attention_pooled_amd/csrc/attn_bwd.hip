@@ -372,16 +372,20 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   // One step: loads of stage st+1 into the next slot, producer on stage st, consumer on
   // stage st-1.  Each job runs its own copy of the loop (same barriers), so that neither
   // keeps the other's loop-invariant addresses alive.
+// The query block of the next stage is read from LDS one step ahead and taken into a
+// scalar register after the barrier, so that no step waits for that read.
 #define SPA_DKDV_LOOP(...)                                                                   \
   {                                                                                        \
     int cur = 0, prev = 2;                                                                 \
+    int qn = list_at(1);                                                                   \
     for (int st = 0; st <= nst; ++st) {                                                    \
       const int nxt = cur == 2 ? 0 : cur + 1;                                              \
-      if (st + 1 < nst)                                                                    \
-        dkdv_load_stage<D, BQ>(src, list_at(st + 1), st + 1, w, lane, tiles[nxt], side[nxt]); \
+      if (st + 1 < nst) dkdv_load_stage<D, BQ>(src, qn, st + 1, w, lane, tiles[nxt], side[nxt]); \
+      const int qn_v = lst[max(0, min((st + 2) / HPB, cnt - 1))];                           \
       __VA_ARGS__;                                                                         \
       wait_vmem();                                                                         \
       __syncthreads();                                                                     \
+      qn = __builtin_amdgcn_readfirstlane(qn_v);                                           \
       prev = cur;                                                                          \
       cur = nxt;                                                                           \
     }                                                                                      \
@@ -640,17 +644,21 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   // the tile body after the loop, so that the loop carries no per-element selects
   const bool tail_last = cnt > 0 && blk(cnt - 1) * kBlkK + kBlkK > N;
   const int cnt_main = cnt - (tail_last ? 1 : 0);
+  // the block index of the next tile is read from LDS one tile ahead and taken into a
+  // scalar register after the barrier, so that no step waits for that read
+  int jn = cnt > 1 ? blk(1) : 0;
   for (int t = 0; t < cnt_main; ++t) {
     const int buf = t & 1;
     if (t + 1 < cnt) {  // the next tile streams into the other buffer meanwhile
-      const int jn = blk(t + 1);
       tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0]);
       tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, jn * kBlkK, smem[buf ^ 1][1]);
     }
-    dq_tile<D, false>(smem[buf][0], smem[buf][1], blk(t) * kBlkK, N, qf, df, lse2, dq_sum, acc,
-                      scale_log2, lane);
+    const int jn_v = lst[min(t + 2, cnt - 1)];
+    dq_tile<D, false>(smem[buf][0], smem[buf][1], 0 /* read by the tail form only */, N, qf,
+                      df, lse2, dq_sum, acc, scale_log2, lane);
     wait_vmem();
     __syncthreads();
+    jn = __builtin_amdgcn_readfirstlane(jn_v);
   }
   if (tail_last) {
     const int buf = cnt_main & 1;

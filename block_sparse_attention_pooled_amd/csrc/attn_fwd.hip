@@ -223,19 +223,24 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   __syncthreads();
   const bool tail_last = cnt > 0 && blk(cnt - 1) * kBlkK + kBlkK > N;
   const int cnt_main = cnt - (tail_last ? 1 : 0);
+  // the block index of the next tile is read from LDS one tile ahead and taken into a
+  // scalar register after the barrier, so that no step waits for that read
 #define SPA_FWD_LOOP(V16_)                                                                   \
   {                                                                                        \
+    int jn = cnt > 1 ? blk(1) : 0;                                                         \
     for (int t = 0; t < cnt_main; ++t) {                                                   \
       const int buf = t & 1;                                                               \
       if (t + 1 < cnt) {                                                                   \
-        const int jn = blk(t + 1);                                                         \
         tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0]);          \
         tile_load_lds_rsrc<D, kBlkK, NT / 64>(vsrc, jn * kBlkK, smem[buf ^ 1][1]);         \
       }                                                                                    \
-      fwd_tile<D, SPLIT, false, V16_>(smem[buf][0], smem[buf][1], blk(t) * kBlkK, N, qf,   \
-                                      oacc, m_run, l_run, scale_log2, lane);               \
+      const int jn_v = lst[min(t + 2, cnt - 1)];                                           \
+      /* key0 is read by the tail form only */                                            \
+      fwd_tile<D, SPLIT, false, V16_>(smem[buf][0], smem[buf][1], 0, N, qf, oacc, m_run,   \
+                                      l_run, scale_log2, lane);                            \
       wait_vmem();                                                                         \
       __syncthreads();                                                                     \
+      jn = __builtin_amdgcn_readfirstlane(jn_v);                                           \
     }                                                                                      \
     if (tail_last) {                                                                       \
       const int buf = cnt_main & 1;                                                        \
