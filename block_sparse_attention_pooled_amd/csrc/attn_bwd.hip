@@ -510,6 +510,12 @@ __device__ __forceinline__ void dq_tile(const uint16_t* Ks, const uint16_t* Vs, 
         dp = mfma32(va[u], df[k0 + u], dp);
       }
     }
+    // the K^T fragments of the first half of dQ += dS K do not depend on the softmax:
+    // their transpose reads are issued first and land while the exponentials run
+    bf16x8 kt0[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) kt0[db] = lds_colfrag<D>(Ks, 32 * kb, 32 * db, lane);
+    SPA_FENCE();
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -lse2));
@@ -527,7 +533,8 @@ __device__ __forceinline__ void dq_tile(const uint16_t* Ks, const uint16_t* Vs, 
       split_bf16x8(dp, half, dh, dl);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 kt = lds_colfrag<D>(Ks, 32 * kb + 16 * half, 32 * db, lane);
+        const bf16x8 kt =
+            half == 0 ? kt0[db] : lds_colfrag<D>(Ks, 32 * kb + 16 * half, 32 * db, lane);
         acc[db] = mfma32(kt, dh, acc[db]);
         acc[db] = mfma32(kt, dl, acc[db]);
       }
