@@ -141,7 +141,8 @@ __device__ __forceinline__ void dkdv_load_stage(const DkdvSrc& src, int qb, int 
 template <int D, bool TAIL>
 __device__ __forceinline__ void dkdv_scores(const uint16_t* tq, const float* sd, float* pw,
                                             const bf16x8 (&kf)[D / 16], int r0, int lane,
-                                            float kmask, float scale_log2, f32x16& sacc) {
+                                            float kmask, float scale_log2, f32x16& sacc,
+                                            bf16x8 (&ob0)[D / 32]) {
   constexpr int KS = D / 16;
   const int h = lane >> 5;
   bf16x8 a[KS];
@@ -156,6 +157,10 @@ __device__ __forceinline__ void dkdv_scores(const uint16_t* tq, const float* sd,
   sacc = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) sacc = mfma32(a[kk], kf[kk], sacc);
+  // the dO^T fragments of the first half of dV += P^T dO do not depend on P: their
+  // transpose reads are issued here and land while the exponentials run
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) ob0[db] = lds_colfrag<D>(tq + 64 * D, r0, 32 * db, lane);
   SPA_FENCE();
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -178,14 +183,15 @@ __device__ __forceinline__ void dkdv_scores(const uint16_t* tq, const float* sd,
 // Producer, second half: dV += P^T dO.
 template <int D>
 __device__ __forceinline__ void dkdv_dv(const uint16_t* tq, const f32x16& p, f32x16 (&acc)[D / 32],
-                                        int r0, int lane) {
+                                        int r0, int lane, const bf16x8 (&ob0)[D / 32]) {
   constexpr int DB = D / 32, HR = 64;
   const uint16_t* dOb = tq + HR * D;
 #pragma unroll
   for (int kq = 0; kq < 2; ++kq) {
     bf16x8 ob[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) ob[db] = lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
+    for (int db = 0; db < DB; ++db)
+      ob[db] = kq == 0 ? ob0[db] : lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
     bf16x8 ph, pl;
     split_bf16x8(p, kq, ph, pl);
 #pragma unroll
@@ -200,14 +206,16 @@ __device__ __forceinline__ void dkdv_dv(const uint16_t* tq, const f32x16& p, f32
 // against the fp16 copy of dO held in the stage slot.
 template <int D>
 __device__ __forceinline__ void dkdv_dv16(const uint16_t* tq, const f32x16& p,
-                                          f32x16 (&acc)[D / 32], int r0, int lane) {
+                                          f32x16 (&acc)[D / 32], int r0, int lane,
+                                          const bf16x8 (&ob0)[D / 32]) {
   constexpr int DB = D / 32, HR = 64;
   const uint16_t* dOb = tq + HR * D;
 #pragma unroll
   for (int kq = 0; kq < 2; ++kq) {
     bf16x8 ob[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) ob[db] = lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
+    for (int db = 0; db < DB; ++db)
+      ob[db] = kq == 0 ? ob0[db] : lds_colfrag<D>(dOb, r0 + 16 * kq, 32 * db, lane);
     const f16x8 ph = to_f16x8(p, kq);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -394,16 +402,18 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
     if (role == 0 && tail) {
       SPA_DKDV_LOOP(if (st < nst) {
         f32x16 p;
+        bf16x8 ob0[DB];
         dkdv_scores<D, true>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane,
-                             kmask, scale_log2, p);
-        dkdv_dv16<D>(tiles[cur], p, acc, r0, lane);
+                             kmask, scale_log2, p, ob0);
+        dkdv_dv16<D>(tiles[cur], p, acc, r0, lane, ob0);
       })
     } else if (role == 0) {
       SPA_DKDV_LOOP(if (st < nst) {
         f32x16 p;
+        bf16x8 ob0[DB];
         dkdv_scores<D, false>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane,
-                              kmask, scale_log2, p);
-        dkdv_dv16<D>(tiles[cur], p, acc, r0, lane);
+                              kmask, scale_log2, p, ob0);
+        dkdv_dv16<D>(tiles[cur], p, acc, r0, lane, ob0);
       })
     } else {
 #pragma unroll
@@ -422,16 +432,18 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   } else if (role == 0 && tail) {  // keys at or beyond N exist only in the last key block
     SPA_DKDV_LOOP(if (st < nst) {
       f32x16 p;
+      bf16x8 ob0[DB];
       dkdv_scores<D, true>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane,
-                           kmask, scale_log2, p);
-      dkdv_dv<D>(tiles[cur], p, acc, r0, lane);
+                           kmask, scale_log2, p, ob0);
+      dkdv_dv<D>(tiles[cur], p, acc, r0, lane, ob0);
     })
   } else if (role == 0) {
     SPA_DKDV_LOOP(if (st < nst) {
       f32x16 p;
+      bf16x8 ob0[DB];
       dkdv_scores<D, false>(tiles[cur], side[cur], pbuf[st & 1] + unit * 1024, bf, r0, lane,
-                            kmask, scale_log2, p);
-      dkdv_dv<D>(tiles[cur], p, acc, r0, lane);
+                            kmask, scale_log2, p, ob0);
+      dkdv_dv<D>(tiles[cur], p, acc, r0, lane, ob0);
     })
   } else {
     SPA_DKDV_LOOP(if (st >= 1) {
