@@ -101,11 +101,13 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
       if (r + 32 >= lim) sc[1][e] = -INFINITY;
     }
   }
-  // the V^T fragments of the first k-step of P*V do not depend on the softmax: their
+  // the V^T fragments of the first two k-steps of P*V do not depend on the softmax: their
   // transpose reads are issued first and land while the exponentials run
-  bf16x8 va0[DB];
+  bf16x8 va0[2][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) va0[db] = lds_colfrag<D>(Vs, 0, 32 * db, lane);
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) va0[kk][db] = lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
   SPA_FENCE();
   // ---- online softmax (log2 domain, scale folded into the exponent) --------------------
   float mloc = sc[0][0];
@@ -142,7 +144,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
       const f16x8 ph = to_f16x8(sc[kk >> 1], kk & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 va = kk == 0 ? va0[db] : lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
+        const bf16x8 va = kk < 2 ? va0[kk][db] : lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
         oacc[db] = mfma32h(__builtin_bit_cast(f16x8, va), ph, oacc[db]);
       }
     }
@@ -156,7 +158,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
         ph = to_bf16x8(sc[kk >> 1], kk & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 va = kk == 0 ? va0[db] : lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
+        const bf16x8 va = kk < 2 ? va0[kk][db] : lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
         oacc[db] = mfma32(va, ph, oacc[db]);
         if constexpr (SPLIT) oacc[db] = mfma32(va, pl, oacc[db]);
       }
