@@ -5,9 +5,13 @@ build_mask (pool + select) -> sparse forward (with the O residual) -> sparse bac
 (D and column lists, dK/dV, dQ).  Default workload: the Wan2.1-1.3B-480p-shaped layer
 (B=1, H=12, N=32760 on a 21x30x52 grid, d=128, blocks 128x64, k=5 %, p=0.9).
 
+The forward's preparation (the fp16 copy of V, which reads V only) runs on a second
+stream during the mask selection; the attention waits for it.
+
 Prints one JSON line with the step time (ms/layer), the per-stage times measured with
-HIP events on the launch stream, the roofline of the dominant kernel, a dense-mask run
-of the same kernels and the CPU oracle timed on a bounded sample.
+HIP events on the launch stream (and the overlapped preparation on its own stream), the
+roofline of the dominant kernel, a dense-mask run of the same kernels and the CPU
+oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -138,21 +142,37 @@ def main():
     bws = torch.empty(spa.bwd_workspace_bytes(q.shape, w.blk_q, w.blk_k), dtype=torch.uint8,
                       device=dev)
     stream = torch.cuda.current_stream(dev)
+    # the forward's preparation (the fp16 copy of V) reads V only: it runs on a second
+    # stream (default priority) while the mask selection runs, and the attention waits for it
+    side = torch.cuda.Stream(dev)
+    ev_fork, ev_join = torch.cuda.Event(), torch.cuda.Event()
     stage_names = ["mask_pool", "mask_select", "fwd", "bwd_prep", "bwd_dq", "bwd_dkdv"]
+    n_ev = 9  # 0-6 on the launch stream (stage bounds), 7-8 around the preparation
 
     def step(events=None, k_frac=w.k_frac, p=w.p):
-        def mark(idx):
+        def mark(idx, st=stream):
             if events is not None:
-                events[idx].record(stream)
+                events[idx].record(st)
         mark(0)
         spa.build_mask(q, k, w.blk_q, w.blk_k, k_frac, p, out=(kv_idx, kv_cnt, None),
                        workspace=mws, stages=spa.MASK_POOL)
         mark(1)
+        # forked after the pooling (which, like the conversion, streams from HBM), so that
+        # the conversion overlaps the selection, whose time is the latency of its rows
+        ev_fork.record(stream)
+        side.wait_event(ev_fork)
+        with torch.cuda.stream(side):
+            mark(7, side)
+            spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k, with_residual=True,
+                                out=(o, lse, o_lo), workspace=fws, stages=spa.FWD_PREP)
+            mark(8, side)
+        ev_join.record(side)
         spa.build_mask(q, k, w.blk_q, w.blk_k, k_frac, p, out=(kv_idx, kv_cnt, None),
                        workspace=mws, stages=spa.MASK_SELECT)
         mark(2)
+        stream.wait_event(ev_join)
         spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k, with_residual=True,
-                            out=(o, lse, o_lo), workspace=fws)
+                            out=(o, lse, o_lo), workspace=fws, stages=spa.FWD_ATTN)
         mark(3)
         for st, idx in ((spa.BWD_PREP, 4), (spa.BWD_DQ, 5), (spa.BWD_DKDV, 6)):
             spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k, o_lo=o_lo,
@@ -163,7 +183,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -174,6 +194,8 @@ def main():
     stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1])
                                      for s in range(args.steps)]))
                 for i, name in enumerate(stage_names)}
+    stage_ms["fwd_prep_overlapped"] = float(np.mean([ev[s][7].elapsed_time(ev[s][8])
+                                                     for s in range(args.steps)]))
     event_step_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][6]) for s in range(args.steps)]))
     log(f"[bench] {ms_per_step:.3f} ms/step (events {event_step_ms:.3f}); stages {stage_ms}")
 
@@ -197,15 +219,28 @@ def main():
     from block_sparse_attention_pooled_amd import traffic as traffic_rec
     roofline = {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": traffic_rec.load(dom, w.name)}
-    attn_ms = stage_ms["fwd"] + stage_ms["bwd_prep"] + stage_ms["bwd_dkdv"] + stage_ms["bwd_dq"]
-    mask_ms = stage_ms["mask_pool"] + stage_ms["mask_select"]
+    # the attention kernels' own times, the overlapped preparation included (the step time
+    # shows what the overlap saves)
+    attn_ms = (stage_ms["fwd"] + stage_ms["fwd_prep_overlapped"] + stage_ms["bwd_prep"]
+               + stage_ms["bwd_dkdv"] + stage_ms["bwd_dq"])
+    mask_in_step_ms = stage_ms["mask_pool"] + stage_ms["mask_select"]
+    # the mask kernels alone (pool + select back to back, nothing on the second stream):
+    # inside a step the selection shares the GPU with the forward's preparation
+    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        mev[s_][0].record(stream)
+        spa.build_mask(q, k, w.blk_q, w.blk_k, w.k_frac, w.p, out=(kv_idx, kv_cnt, None),
+                       workspace=mws)
+        mev[s_][1].record(stream)
+    torch.cuda.synchronize()
+    mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in mev]))
 
     # ---- cold-cache steps: reading 512 MB evicts the 256 MB last-level cache before each
     # step (a read, so that no dirty lines are written back during the step) -------------
     cold = None
     if args.cold_steps > 0:
         flush = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
                for _ in range(args.cold_steps)]
         for s_ in range(args.cold_steps):
             float(flush.sum())
@@ -275,7 +310,8 @@ def main():
                    "blk_k": w.blk_k, "k_frac": w.k_frac, "p": w.p, "alpha": w.alpha,
                    "grid": list(w.grid) if w.grid else None, "density": density,
                    "grad_dtype": "fp32"},
-        "stage_ms": stage_ms, "mask_ms": mask_ms, "attn_fwd_bwd_ms": attn_ms,
+        "stage_ms": stage_ms, "mask_ms": mask_ms, "mask_in_step_ms": mask_in_step_ms,
+        "attn_fwd_bwd_ms": attn_ms,
         "credited_tflops_fwd_bwd": fl_total / (attn_ms * 1e-3) / 1e12,
         "mfma_util_credited": fl_total / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "mask_hbm_frac": mask_bytes / (mask_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,

@@ -28,10 +28,11 @@ _LIB_NAME = "libspa.so"
 _lib = None
 
 SYMBOLS = ("spa_mask_workspace_bytes", "spa_build_mask", "spa_build_mask_stages",
-           "spa_fwd_workspace_bytes", "spa_sparse_attn_fwd", "spa_bwd_workspace_bytes",
-           "spa_sparse_attn_bwd", "spa_sparse_attn_bwd_stages", "spa_status_string",
-           "spa_version")
+           "spa_fwd_workspace_bytes", "spa_sparse_attn_fwd", "spa_sparse_attn_fwd_stages",
+           "spa_bwd_workspace_bytes", "spa_sparse_attn_bwd", "spa_sparse_attn_bwd_stages",
+           "spa_status_string", "spa_version")
 MASK_POOL, MASK_SELECT, MASK_ALL = 1, 2, 3
+FWD_PREP, FWD_ATTN, FWD_ALL = 1, 2, 3
 BWD_PREP, BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 4, 7
 
 
@@ -75,6 +76,9 @@ def load_library():
     lib.spa_build_mask_stages.restype = ctypes.c_int
     lib.spa_sparse_attn_fwd.argtypes = [dp, vp, vp, vp, i32p, i32p, ctypes.c_double, vp, vp, vp,
                                         vp, sz, vp]
+    lib.spa_sparse_attn_fwd_stages.argtypes = [dp, vp, vp, vp, i32p, i32p, ctypes.c_double, vp,
+                                               vp, vp, vp, sz, ctypes.c_uint, vp]
+    lib.spa_sparse_attn_fwd_stages.restype = ctypes.c_int
     lib.spa_fwd_workspace_bytes.argtypes = [dp]
     lib.spa_fwd_workspace_bytes.restype = sz
     lib.spa_sparse_attn_fwd.restype = ctypes.c_int
@@ -183,13 +187,15 @@ def build_mask(q, k, blk_q: int = 128, blk_k: int = 64, k_frac: float = 0.05, p:
 
 def sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, blk_q: int = 128, blk_k: int = 64,
                     scale: float | None = None, with_residual: bool = False, out=None,
-                    workspace=None):
+                    workspace=None, stages: int = FWD_ALL):
     """Block-sparse attention forward.
 
     Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N]), or (o, lse, o_lo) with
     ``with_residual=True``: o_lo is the bf16 rounding residual of O that the backward
     pass uses for D = <dO, O>.  The residual mode needs a device workspace of
-    fwd_workspace_bytes() (allocated here when not given).
+    fwd_workspace_bytes() (allocated here when not given).  ``stages`` selects FWD_PREP
+    (the fp16 copy of V into the workspace; it reads V only) and/or FWD_ATTN, which with
+    the residual reads what FWD_PREP wrote into the same workspace.
     """
     torch = _torch()
     lib = load_library()
@@ -215,10 +221,11 @@ def sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, blk_q: int = 128, blk_k: int = 64,
         wsb = lib.spa_fwd_workspace_bytes(ctypes.byref(dims))
         ws = workspace if workspace is not None else torch.empty(max(1, wsb), dtype=torch.uint8,
                                                                 device=q.device)
-    rc = lib.spa_sparse_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx),
-                                 _ptr(kv_cnt), float(scale or 0.0), _ptr(o), _ptr(o_lo),
-                                 _ptr(lse), _ptr(ws), ws.numel() if ws is not None else 0,
-                                 _stream(q.device))
+    rc = lib.spa_sparse_attn_fwd_stages(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(kv_idx), _ptr(kv_cnt), float(scale or 0.0), _ptr(o),
+                                        _ptr(o_lo), _ptr(lse), _ptr(ws),
+                                        ws.numel() if ws is not None else 0, int(stages),
+                                        _stream(q.device))
     _check("spa_sparse_attn_fwd", rc)
     return (o, lse, o_lo) if with_residual else (o, lse)
 

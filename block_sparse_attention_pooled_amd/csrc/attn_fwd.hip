@@ -287,17 +287,19 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
 }
 
 template <int D, int BQ>
-static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
+static hipError_t launch_fwd_t(const FwdArgs& a, unsigned stages, hipStream_t s) {
   const Geometry& g = a.g;
   const int total = (int)(g.nqb * g.bh());
   dim3 grid(total);
   if (a.o_lo) {
-    hipLaunchKernelGGL((k_vconv<D>), dim3(g.nkb, (unsigned)g.bh()), dim3(256), 0, s, a.v, a.v16,
-                       g.N, g.nkb, a.vflag);
-    hipLaunchKernelGGL((k_fwd<D, BQ, true>), grid, dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.v16,
-                       a.vflag, a.kv_idx, a.kv_cnt, g.N, g.nqb, g.nkb, total, a.scale * kLog2e,
-                       a.o, a.o_lo, a.lse);
-  } else {
+    if (stages & 1u)
+      hipLaunchKernelGGL((k_vconv<D>), dim3(g.nkb, (unsigned)g.bh()), dim3(256), 0, s, a.v,
+                         a.v16, g.N, g.nkb, a.vflag);
+    if (stages & 2u)
+      hipLaunchKernelGGL((k_fwd<D, BQ, true>), grid, dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.v16,
+                         a.vflag, a.kv_idx, a.kv_cnt, g.N, g.nqb, g.nkb, total,
+                         a.scale * kLog2e, a.o, a.o_lo, a.lse);
+  } else if (stages & 2u) {
     hipLaunchKernelGGL((k_fwd<D, BQ, false>), grid, dim3(BQ * 2), 0, s, a.q, a.k, a.v,
                        (const uint16_t*)nullptr, (const int32_t*)nullptr, a.kv_idx, a.kv_cnt,
                        g.N, g.nqb, g.nkb, total, a.scale * kLog2e, a.o, a.o_lo, a.lse);
@@ -316,12 +318,12 @@ void fwd_workspace_carve(const Geometry& g, void* ws, FwdArgs* a) {
   a->vflag = reinterpret_cast<int32_t*>(p);
 }
 
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd(const FwdArgs& a, unsigned stages, hipStream_t s) {
   const int d = a.g.d, bq = a.g.blk_q;
-  if (d == 128 && bq == 128) return launch_fwd_t<128, 128>(a, s);
-  if (d == 128 && bq == 64) return launch_fwd_t<128, 64>(a, s);
-  if (d == 64 && bq == 128) return launch_fwd_t<64, 128>(a, s);
-  return launch_fwd_t<64, 64>(a, s);
+  if (d == 128 && bq == 128) return launch_fwd_t<128, 128>(a, stages, s);
+  if (d == 128 && bq == 64) return launch_fwd_t<128, 64>(a, stages, s);
+  if (d == 64 && bq == 128) return launch_fwd_t<64, 128>(a, stages, s);
+  return launch_fwd_t<64, 64>(a, stages, s);
 }
 
 }  // namespace spa

@@ -98,9 +98,18 @@ size_t spa_fwd_workspace_bytes(const spa_dims* dims) {
 int spa_sparse_attn_fwd(const spa_dims* dims, const void* q, const void* k, const void* v,
                         const int32_t* kv_idx, const int32_t* kv_cnt, double scale, void* o,
                         void* o_lo, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return spa_sparse_attn_fwd_stages(dims, q, k, v, kv_idx, kv_cnt, scale, o, o_lo, lse, ws,
+                                    ws_bytes, SPA_FWD_ALL, stream);
+}
+
+int spa_sparse_attn_fwd_stages(const spa_dims* dims, const void* q, const void* k,
+                               const void* v, const int32_t* kv_idx, const int32_t* kv_cnt,
+                               double scale, void* o, void* o_lo, float* lse, void* ws,
+                               size_t ws_bytes, unsigned stages, void* stream) {
   Geometry g;
   int rc = check_dims(dims, &g);
   if (rc != SPA_OK) return rc;
+  if (stages == 0u || (stages & ~(unsigned)SPA_FWD_ALL)) return SPA_E_PARAM;
   if (!q || !k || !v || !kv_idx || !kv_cnt || !o || !lse) return SPA_E_NULL;
   if (o_lo && !ws) return SPA_E_NULL;
   if (std::isnan(scale) || std::isinf(scale)) return SPA_E_PARAM;
@@ -119,7 +128,7 @@ int spa_sparse_attn_fwd(const spa_dims* dims, const void* q, const void* k, cons
   a.o = static_cast<uint16_t*>(o);
   a.o_lo = static_cast<uint16_t*>(o_lo);
   a.lse = lse;
-  return launch_status(spa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+  return launch_status(spa::launch_fwd(a, stages, static_cast<hipStream_t>(stream)));
 }
 
 size_t spa_bwd_workspace_bytes(const spa_dims* dims) {

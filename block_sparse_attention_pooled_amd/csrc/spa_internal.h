@@ -50,7 +50,8 @@ struct FwdArgs {
 };
 size_t fwd_workspace_bytes(const Geometry& g);
 void fwd_workspace_carve(const Geometry& g, void* ws, FwdArgs* a);
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
+// stage bits: 1 = the fp16 copy of V (with o_lo only), 2 = the attention
+hipError_t launch_fwd(const FwdArgs& a, unsigned stages, hipStream_t s);
 
 // ---- backward -----------------------------------------------------------------------
 struct BwdArgs {

@@ -178,13 +178,18 @@ SPA_API int spa_sparse_attn_bwd(const spa_dims* dims, const void* q, const void*
  * in one call or several with the same arguments and workspace, equals the unstaged
  * call).  Stage bits of spa_build_mask_stages: SPA_MASK_POOL (block means of Q and K
  * into the workspace), SPA_MASK_SELECT (pooled softmax and selection from the
- * workspace).  Stage bits of spa_sparse_attn_bwd_stages: SPA_BWD_PREP (the
+ * workspace).  Stage bits of spa_sparse_attn_fwd_stages: SPA_FWD_PREP (with o_lo, the
+ * fp16 copy of V and its per-block flags, into the workspace; it reads V only, so a caller
+ * may run it on a second stream while the mask is built; without o_lo it launches
+ * nothing), SPA_FWD_ATTN (the attention; with o_lo it reads what SPA_FWD_PREP wrote from
+ * the same V).  Stage bits of spa_sparse_attn_bwd_stages: SPA_BWD_PREP (the
  * per-key-block query-block lists and the order in which their workgroups run, into the
  * workspace), SPA_BWD_DQ (dQ; also writes D and lse * log2(e) of every row and the fp16
  * copy of dO into the workspace), SPA_BWD_DKDV (dK, dV; reads what the other two wrote).  A zero or unknown stage mask gives SPA_E_PARAM.
  */
 enum {
   SPA_MASK_POOL = 1, SPA_MASK_SELECT = 2, SPA_MASK_ALL = 3,
+  SPA_FWD_PREP = 1, SPA_FWD_ATTN = 2, SPA_FWD_ALL = 3,
   SPA_BWD_PREP = 1, SPA_BWD_DQ = 2, SPA_BWD_DKDV = 4, SPA_BWD_ALL = 7
 };
 
@@ -192,6 +197,12 @@ SPA_API int spa_build_mask_stages(const spa_dims* dims, const void* q, const voi
                                   double k_frac, double p, double pooled_scale, int32_t* kv_idx,
                                   int32_t* kv_cnt, int32_t* rule_len, void* ws, size_t ws_bytes,
                                   unsigned stages, void* stream);
+
+SPA_API int spa_sparse_attn_fwd_stages(const spa_dims* dims, const void* q, const void* k,
+                                       const void* v, const int32_t* kv_idx,
+                                       const int32_t* kv_cnt, double scale, void* o, void* o_lo,
+                                       float* lse, void* ws, size_t ws_bytes, unsigned stages,
+                                       void* stream);
 
 SPA_API int spa_sparse_attn_bwd_stages(const spa_dims* dims, const void* q, const void* k,
                                        const void* v, const void* o, const void* o_lo,

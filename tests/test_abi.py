@@ -124,6 +124,19 @@ def test_bad_scales_and_grad_dtype_rejected():
                                    1 << 40, None) == -3
 
 
+@pytest.mark.parametrize("stages", [0, 4, 8, 0xFFFFFFFF])
+def test_bad_stage_masks_rejected(stages):
+    lib = spa.load_library()
+    d = _dims()
+    assert lib.spa_sparse_attn_fwd_stages(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE,
+                                          None, FAKE, None, 0, stages, None) == -3
+    assert lib.spa_build_mask_stages(ctypes.byref(d), FAKE, FAKE, 0.05, 0.9, 0.0, FAKE, FAKE,
+                                     None, FAKE, 1 << 40, stages, None) == -3
+    if stages != 4:  # 4 is SPA_BWD_DKDV
+        assert lib.spa_sparse_attn_bwd_stages(ctypes.byref(d), *([FAKE] * 9), 0.0, FAKE, FAKE,
+                                              FAKE, 0, FAKE, 1 << 40, stages, None) == -3
+
+
 def test_small_workspace_rejected():
     lib = spa.load_library()
     d = _dims()

@@ -272,6 +272,32 @@ def test_small_v_and_do_keep_relative_precision(torch_gpu):
     assert err_v <= 1.0
 
 
+def test_forward_stages_on_two_streams_match_the_whole_call(torch_gpu):
+    """The forward's preparation (the fp16 copy of V) run on a second stream, then the
+    attention on the first after a join, equals the unstaged call bit for bit."""
+    torch = torch_gpu
+    w = small_workload(1000, 128, 128, grid=(2, 20, 25), B=2, H=3)
+    g = synth.generate(w)
+    q, k, v = (to_dev(torch, g[n]) for n in ("q", "k", "v"))
+    kv_idx, kv_cnt = spa.build_mask(q, k, w.blk_q, w.blk_k, w.k_frac, w.p)
+    o1, l1, r1 = spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                                     with_residual=True)
+    o2, l2, r2 = torch.empty_like(o1), torch.empty_like(l1), torch.empty_like(r1)
+    ws = torch.empty(spa.fwd_workspace_bytes(q.shape, w.blk_q, w.blk_k), dtype=torch.uint8,
+                     device=q.device)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k, with_residual=True,
+                            out=(o2, l2, r2), workspace=ws, stages=spa.FWD_PREP)
+    main.wait_stream(side)
+    spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k, with_residual=True,
+                        out=(o2, l2, r2), workspace=ws, stages=spa.FWD_ATTN)
+    torch.cuda.synchronize()
+    for a, b in ((o1, o2), (l1, l2), (r1, r2)):
+        assert torch.equal(a, b)
+
+
 def test_determinism(torch_gpu):
     torch = torch_gpu
     w = small_workload(1000, 128, 128, grid=(2, 20, 25), B=2, H=3)
