@@ -250,6 +250,9 @@ def main():
         cold_stage = {name: float(np.mean([cev[s_][i].elapsed_time(cev[s_][i + 1])
                                            for s_ in range(args.cold_steps)]))
                       for i, name in enumerate(stage_names)}
+        cold_stage["fwd_prep_overlapped"] = float(np.mean([cev[s_][7].elapsed_time(cev[s_][8])
+                                                          for s_ in range(args.cold_steps)]))
+        # the mask's rate here is its time inside the step (beside the copy of V)
         cold = {"ms_per_step": float(np.mean([cev[s_][0].elapsed_time(cev[s_][6])
                                               for s_ in range(args.cold_steps)])),
                 "stage_ms": cold_stage,
