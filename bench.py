@@ -2,14 +2,15 @@
 
 One step = the whole hot path on one synthetic layer with inputs resident in HBM:
 build_mask (pool + select) -> sparse forward (with the O residual) -> sparse backward
-(D and column lists, dK/dV, dQ).  Default workload: the Wan2.1-1.3B-480p-shaped layer
+(column lists, dQ with D, dK/dV).  Default workload: the Wan2.1-1.3B-480p-shaped layer
 (B=1, H=12, N=32760 on a 21x30x52 grid, d=128, blocks 128x64, k=5 %, p=0.9).
 
-The forward's preparation (the fp16 copy of V, which reads V only) runs on a second
-stream during the mask selection; the attention waits for it.
+Two preparations run on a second stream: the forward's fp16 copy of V (it reads V only)
+during the mask selection, and the backward's column lists (they read the mask only)
+during the forward.  Each consumer waits for its preparation.
 
 Prints one JSON line with the step time (ms/layer), the per-stage times measured with
-HIP events on the launch stream (and the overlapped preparation on its own stream), the
+HIP events on the stream each stage runs on, the
 roofline of the dominant kernel, a dense-mask run of the same kernels and the CPU
 oracle timed on a bounded sample.
 """
@@ -142,12 +143,16 @@ def main():
     bws = torch.empty(spa.bwd_workspace_bytes(q.shape, w.blk_q, w.blk_k), dtype=torch.uint8,
                       device=dev)
     stream = torch.cuda.current_stream(dev)
-    # the forward's preparation (the fp16 copy of V) reads V only: it runs on a second
-    # stream (default priority) while the mask selection runs, and the attention waits for it
+    # Two preparation stages run on a second stream (default priority) beside the launch
+    # stream: the forward's fp16 copy of V reads V only and runs during the mask selection;
+    # the backward's column lists read the mask only and are built during the forward.
     side = torch.cuda.Stream(dev)
     ev_fork, ev_join = torch.cuda.Event(), torch.cuda.Event()
-    stage_names = ["mask_pool", "mask_select", "fwd", "bwd_prep", "bwd_dq", "bwd_dkdv"]
-    n_ev = 9  # 0-6 on the launch stream (stage bounds), 7-8 around the preparation
+    ev_fork2, ev_join2 = torch.cuda.Event(), torch.cuda.Event()
+    stage_names = ["mask_pool", "mask_select", "fwd", "bwd_dq", "bwd_dkdv"]
+    # events 0-5 bound the launch stream's stages; 6-7 and 8-9 bound the two preparations
+    side_stages = {"fwd_prep_overlapped": 6, "bwd_prep_overlapped": 8}
+    n_ev = 10
 
     def step(events=None, k_frac=w.k_frac, p=w.p):
         def mark(idx, st=stream):
@@ -162,19 +167,28 @@ def main():
         ev_fork.record(stream)
         side.wait_event(ev_fork)
         with torch.cuda.stream(side):
-            mark(7, side)
+            mark(6, side)
             spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k, with_residual=True,
                                 out=(o, lse, o_lo), workspace=fws, stages=spa.FWD_PREP)
-            mark(8, side)
+            mark(7, side)
         ev_join.record(side)
         spa.build_mask(q, k, w.blk_q, w.blk_k, k_frac, p, out=(kv_idx, kv_cnt, None),
                        workspace=mws, stages=spa.MASK_SELECT)
         mark(2)
+        ev_fork2.record(stream)
+        side.wait_event(ev_fork2)
+        with torch.cuda.stream(side):
+            mark(8, side)
+            spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k, o_lo=o_lo,
+                                out=(dq, dk, dv), workspace=bws, stages=spa.BWD_PREP)
+            mark(9, side)
+        ev_join2.record(side)
         stream.wait_event(ev_join)
         spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k, with_residual=True,
                             out=(o, lse, o_lo), workspace=fws, stages=spa.FWD_ATTN)
         mark(3)
-        for st, idx in ((spa.BWD_PREP, 4), (spa.BWD_DQ, 5), (spa.BWD_DKDV, 6)):
+        stream.wait_event(ev_join2)
+        for st, idx in ((spa.BWD_DQ, 4), (spa.BWD_DKDV, 5)):
             spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k, o_lo=o_lo,
                                 out=(dq, dk, dv), workspace=bws, stages=st)
             mark(idx)
@@ -194,9 +208,10 @@ def main():
     stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1])
                                      for s in range(args.steps)]))
                 for i, name in enumerate(stage_names)}
-    stage_ms["fwd_prep_overlapped"] = float(np.mean([ev[s][7].elapsed_time(ev[s][8])
-                                                     for s in range(args.steps)]))
-    event_step_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][6]) for s in range(args.steps)]))
+    for name, i in side_stages.items():
+        stage_ms[name] = float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1])
+                                        for s in range(args.steps)]))
+    event_step_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][5]) for s in range(args.steps)]))
     log(f"[bench] {ms_per_step:.3f} ms/step (events {event_step_ms:.3f}); stages {stage_ms}")
 
     # ---- algorithmic work ---------------------------------------------------------------
@@ -221,7 +236,7 @@ def main():
                 "frac": achieved / peak, "traffic": traffic_rec.load(dom, w.name)}
     # the attention kernels' own times, the overlapped preparation included (the step time
     # shows what the overlap saves)
-    attn_ms = (stage_ms["fwd"] + stage_ms["fwd_prep_overlapped"] + stage_ms["bwd_prep"]
+    attn_ms = (stage_ms["fwd"] + stage_ms["fwd_prep_overlapped"] + stage_ms["bwd_prep_overlapped"]
                + stage_ms["bwd_dkdv"] + stage_ms["bwd_dq"])
     mask_in_step_ms = stage_ms["mask_pool"] + stage_ms["mask_select"]
     # the mask kernels alone (pool + select back to back, nothing on the second stream):
@@ -250,10 +265,11 @@ def main():
         cold_stage = {name: float(np.mean([cev[s_][i].elapsed_time(cev[s_][i + 1])
                                            for s_ in range(args.cold_steps)]))
                       for i, name in enumerate(stage_names)}
-        cold_stage["fwd_prep_overlapped"] = float(np.mean([cev[s_][7].elapsed_time(cev[s_][8])
-                                                          for s_ in range(args.cold_steps)]))
+        for name, i in side_stages.items():
+            cold_stage[name] = float(np.mean([cev[s_][i].elapsed_time(cev[s_][i + 1])
+                                              for s_ in range(args.cold_steps)]))
         # the mask's rate here is its time inside the step (beside the copy of V)
-        cold = {"ms_per_step": float(np.mean([cev[s_][0].elapsed_time(cev[s_][6])
+        cold = {"ms_per_step": float(np.mean([cev[s_][0].elapsed_time(cev[s_][5])
                                               for s_ in range(args.cold_steps)])),
                 "stage_ms": cold_stage,
                 "mask_hbm_frac": mask_bytes / ((cold_stage["mask_pool"] + cold_stage["mask_select"])

@@ -184,8 +184,11 @@ SPA_API int spa_sparse_attn_bwd(const spa_dims* dims, const void* q, const void*
  * nothing), SPA_FWD_ATTN (the attention; with o_lo it reads what SPA_FWD_PREP wrote from
  * the same V).  Stage bits of spa_sparse_attn_bwd_stages: SPA_BWD_PREP (the
  * per-key-block query-block lists and the order in which their workgroups run, into the
- * workspace), SPA_BWD_DQ (dQ; also writes D and lse * log2(e) of every row and the fp16
- * copy of dO into the workspace), SPA_BWD_DKDV (dK, dV; reads what the other two wrote).  A zero or unknown stage mask gives SPA_E_PARAM.
+ * workspace; it reads kv_idx and kv_cnt only, so a caller may run it on a second stream
+ * once the mask exists, e.g. during the forward), SPA_BWD_DQ (dQ; also writes D and
+ * lse * log2(e) of every row and the fp16 copy of dO into the workspace), SPA_BWD_DKDV
+ * (dK, dV; reads what the other two wrote).  A zero or unknown stage mask gives
+ * SPA_E_PARAM.
  */
 enum {
   SPA_MASK_POOL = 1, SPA_MASK_SELECT = 2, SPA_MASK_ALL = 3,

@@ -298,6 +298,39 @@ def test_forward_stages_on_two_streams_match_the_whole_call(torch_gpu):
         assert torch.equal(a, b)
 
 
+def test_column_lists_built_beside_the_forward_match_the_whole_call(torch_gpu):
+    """The backward's column lists built on a second stream while the forward runs on the
+    first (the two read nothing the other writes), then dQ and dK/dV after a join, equal
+    the unstaged backward bit for bit."""
+    torch = torch_gpu
+    w = small_workload(1000, 128, 128, grid=(2, 20, 25), B=2, H=3)
+    g = synth.generate(w)
+    q, k, v, do = (to_dev(torch, g[n]) for n in ("q", "k", "v", "do"))
+    kv_idx, kv_cnt = spa.build_mask(q, k, w.blk_q, w.blk_k, w.k_frac, w.p)
+    o, lse, o_lo = spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                                       with_residual=True)
+    want = spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                               o_lo=o_lo)
+    o2, l2, r2 = torch.empty_like(o), torch.empty_like(lse), torch.empty_like(o_lo)
+    got = tuple(torch.empty_like(x) for x in want)
+    bws = torch.empty(spa.bwd_workspace_bytes(q.shape, w.blk_q, w.blk_k), dtype=torch.uint8,
+                      device=q.device)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        spa.sparse_attn_bwd(q, k, v, o2, do, l2, kv_idx, kv_cnt, w.blk_q, w.blk_k, o_lo=r2,
+                            out=got, workspace=bws, stages=spa.BWD_PREP)
+    spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k, with_residual=True,
+                        out=(o2, l2, r2))
+    main.wait_stream(side)
+    for st in (spa.BWD_DQ, spa.BWD_DKDV):
+        spa.sparse_attn_bwd(q, k, v, o2, do, l2, kv_idx, kv_cnt, w.blk_q, w.blk_k, o_lo=r2,
+                            out=got, workspace=bws, stages=st)
+    torch.cuda.synchronize()
+    for a, b in zip(want, got):
+        assert torch.equal(a, b)
+
+
 def test_determinism(torch_gpu):
     torch = torch_gpu
     w = small_workload(1000, 128, 128, grid=(2, 20, 25), B=2, H=3)
