@@ -121,6 +121,60 @@ def test_small_parity(torch_gpu, tag, w):
     full_check(torch_gpu, w, w.k_frac, w.p, tag)
 
 
+CALLER_LIST_CASES = [("n1000_d128_q128", small_workload(1000, 128, 128, grid=(2, 20, 25))),
+                     ("n777_d64_q64", small_workload(777, 64, 64, grid=(3, 7, 37)))]
+
+
+@pytest.mark.parametrize("tag,w", CALLER_LIST_CASES, ids=[c[0] for c in CALLER_LIST_CASES])
+def test_caller_supplied_lists_parity(torch_gpu, tag, w):
+    """Lists passed in by the caller, of kinds the mask never emits: a row keeping only the
+    partial last key block (the loop runs no full tile), a row keeping only block 0, a row
+    keeping every block, and random ascending subsets.  Forward and backward against the
+    oracle on the same lists."""
+    torch = torch_gpu
+    B, H, N, d = w.shape()
+    nqb, nkb = -(-N // w.blk_q), -(-N // w.blk_k)
+    rng = np.random.default_rng(11)
+    kv_idx = np.zeros((B, H, nqb, nkb), dtype=np.int32)  # entries past the count unused
+    kv_cnt = np.zeros((B, H, nqb), dtype=np.int32)
+    lists = {}
+    for b in range(B):
+        for h in range(H):
+            rows = []
+            for i in range(nqb):
+                mode = (i + h) % 4
+                if mode == 0:
+                    keep = np.array([nkb - 1])
+                elif mode == 1:
+                    keep = np.array([0])
+                elif mode == 2:
+                    keep = np.arange(nkb)
+                else:
+                    keep = np.sort(rng.choice(nkb, size=int(rng.integers(1, nkb + 1)),
+                                              replace=False))
+                kv_idx[b, h, i, :keep.size] = keep
+                kv_cnt[b, h, i] = keep.size
+                rows.append(keep.astype(np.int64))
+            lists[(b, h)] = rows
+    log(f"[case caller lists {tag}] shape={w.shape()} counts={kv_cnt.ravel().tolist()}")
+    g = synth.generate(w)
+    q, k, v, do = (to_dev(torch, g[n]) for n in ("q", "k", "v", "do"))
+    idx_t, cnt_t = torch.from_numpy(kv_idx).cuda(), torch.from_numpy(kv_cnt).cuda()
+    o, lse, o_lo = spa.sparse_attn_fwd(q, k, v, idx_t, cnt_t, w.blk_q, w.blk_k,
+                                       with_residual=True)
+    dq, dk, dv = spa.sparse_attn_bwd(q, k, v, o, do, lse, idx_t, cnt_t, w.blk_q, w.blk_k,
+                                     o_lo=o_lo)
+    torch.cuda.synchronize()
+    qh, kh, vh, doh = (O.widen_bf16(g[n]) for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = O.sparse_attn_fwd(qh, kh, vh, lists, w.blk_q, w.blk_k)
+    check_close("O", o.float().cpu().numpy(), o_ref)
+    check_close("LSE", lse.cpu().numpy(), lse_ref)
+    dq_ref, dk_ref, dv_ref = O.sparse_attn_bwd(qh, kh, vh, doh, lists, w.blk_q, w.blk_k)
+    check_close("dQ", dq.cpu().numpy(), dq_ref)
+    check_close("dK", dk.cpu().numpy(), dk_ref)
+    check_close("dV", dv.cpu().numpy(), dv_ref)
+
+
 RULES = [(0.1, 0.9), (0.0, 0.7), (0.2, 0.0), (1.0, 0.5), (0.05, 1.0), (0.0, 0.0), (0.3, 0.95)]
 
 
