@@ -146,6 +146,53 @@ int main(int argc, char** argv) {
                              0, bws, bws_bytes, NULL) == SPA_OK, "sparse_attn_bwd");
   CHECK_HIP(hipDeviceSynchronize());
 
+  /* the staged calls, one stage per call into fresh outputs and workspaces, equal the
+     unstaged calls byte for byte; bad stage masks are rejected before any launch */
+  EXPECT(spa_sparse_attn_fwd_stages(&dm, q, k, v, kv_idx, kv_cnt, 0.0, o, o_lo, lse, fws,
+                                    fws_bytes, 0u, NULL) == SPA_E_PARAM, "empty fwd stage mask");
+  EXPECT(spa_sparse_attn_fwd_stages(&dm, q, k, v, kv_idx, kv_cnt, 0.0, o, o_lo, lse, fws,
+                                    fws_bytes, 4u, NULL) == SPA_E_PARAM, "unknown fwd stage bit");
+  EXPECT(spa_sparse_attn_bwd_stages(&dm, q, k, v, o, o_lo, dout, lse, kv_idx, kv_cnt, 0.0, dq,
+                                    dk, dv, 0, bws, bws_bytes, 8u, NULL) == SPA_E_PARAM,
+         "unknown bwd stage bit");
+  void* o2 = dev_alloc(nel * 2);
+  void* o_lo2 = dev_alloc(nel * 2);
+  float* lse2 = (float*)dev_alloc(nrow * 4);
+  void* fws2 = dev_alloc(fws_bytes);
+  const unsigned fwd_st[2] = {SPA_FWD_PREP, SPA_FWD_ATTN};
+  for (int t = 0; t < 2; ++t)
+    EXPECT(spa_sparse_attn_fwd_stages(&dm, q, k, v, kv_idx, kv_cnt, 0.0, o2, o_lo2, lse2, fws2,
+                                      fws_bytes, fwd_st[t], NULL) == SPA_OK,
+           "staged sparse_attn_fwd");
+  void* bws2 = dev_alloc(bws_bytes);
+  float* dq2 = (float*)dev_alloc(nel * 4);
+  float* dk2 = (float*)dev_alloc(nel * 4);
+  float* dv2 = (float*)dev_alloc(nel * 4);
+  const unsigned bwd_st[3] = {SPA_BWD_PREP, SPA_BWD_DQ, SPA_BWD_DKDV};
+  for (int t = 0; t < 3; ++t)
+    EXPECT(spa_sparse_attn_bwd_stages(&dm, q, k, v, o2, o_lo2, dout, lse2, kv_idx, kv_cnt, 0.0,
+                                      dq2, dk2, dv2, 0, bws2, bws_bytes, bwd_st[t], NULL) ==
+               SPA_OK,
+           "staged sparse_attn_bwd");
+  CHECK_HIP(hipDeviceSynchronize());
+  {
+    const void* pairs[][2] = {{o, o2}, {o_lo, o_lo2}, {lse, lse2}, {dq, dq2}, {dk, dk2},
+                              {dv, dv2}};
+    const size_t sizes[] = {nel * 2, nel * 2, nrow * 4, nel * 4, nel * 4, nel * 4};
+    for (int t = 0; t < 6; ++t) {
+      unsigned char* a = (unsigned char*)malloc(sizes[t]);
+      unsigned char* b = (unsigned char*)malloc(sizes[t]);
+      fetch(a, pairs[t][0], sizes[t]);
+      fetch(b, pairs[t][1], sizes[t]);
+      EXPECT(memcmp(a, b, sizes[t]) == 0, "staged calls equal the unstaged ones");
+      free(a);
+      free(b);
+    }
+  }
+  void* staged_bufs[] = {o2, o_lo2, lse2, fws2, bws2, dq2, dk2, dv2};
+  for (size_t i = 0; i < sizeof(staged_bufs) / sizeof(staged_bufs[0]); ++i)
+    CHECK_HIP(hipFree(staged_bufs[i]));
+
   /* results: structural checks here, values compared by the calling test */
   int32_t* h_cnt = (int32_t*)malloc(nlist * 4);
   int32_t* h_idx = (int32_t*)malloc(nlist * nkb * 4);
