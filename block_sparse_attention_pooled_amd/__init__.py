@@ -139,6 +139,32 @@ def _dev_tensor(t, dtype, name):
     return t
 
 
+def _out_tensor(t, dtype, shape, name, device):
+    """A caller-supplied output: the dtype, shape and device the kernels write, contiguous."""
+    _dev_tensor(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    return t
+
+
+def _workspace(ws, need: int, device, name: str):
+    """(tensor, byte count) of a workspace: allocated here when not given, else checked to
+    be a contiguous device tensor of at least `need` bytes."""
+    torch = _torch()
+    if ws is None:
+        return torch.empty(max(1, need), dtype=torch.uint8, device=device), max(1, need)
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"{name} holds {nbytes} bytes; {need} are needed")
+    return ws, nbytes
+
+
 def _stream(dev):
     return ctypes.c_void_p(_torch().cuda.current_stream(dev).cuda_stream)
 
@@ -168,18 +194,25 @@ def build_mask(q, k, blk_q: int = 128, blk_k: int = 64, k_frac: float = 0.05, p:
     B, H, N, d = q.shape
     nqb, nkb = n_blocks(N, blk_q), n_blocks(N, blk_k)
     dims = _dims(q.shape, blk_q, blk_k)
+    if k.device != q.device:
+        raise ValueError("q and k must be on the same device")
     if out is None:
         kv_idx = torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=q.device)
         kv_cnt = torch.empty((B, H, nqb), dtype=torch.int32, device=q.device)
         rl = torch.empty((B, H, nqb, 2), dtype=torch.int32, device=q.device) if rule_len else None
     else:
         kv_idx, kv_cnt, rl = out
-    wsb = lib.spa_mask_workspace_bytes(ctypes.byref(dims))
-    ws = workspace if workspace is not None else torch.empty(max(1, wsb), dtype=torch.uint8,
-                                                            device=q.device)
+        _out_tensor(kv_idx, torch.int32, (B, H, nqb, nkb), "kv_idx", q.device)
+        _out_tensor(kv_cnt, torch.int32, (B, H, nqb), "kv_cnt", q.device)
+        if rule_len and rl is None:
+            raise ValueError("rule_len=True needs a rule_len tensor in out")
+        if rl is not None:
+            _out_tensor(rl, torch.int32, (B, H, nqb, 2), "rule_len", q.device)
+    ws, wsn = _workspace(workspace, int(lib.spa_mask_workspace_bytes(ctypes.byref(dims))),
+                         q.device, "workspace")
     rc = lib.spa_build_mask_stages(ctypes.byref(dims), _ptr(q), _ptr(k), float(k_frac),
                                    float(p), float(pooled_scale or 0.0), _ptr(kv_idx),
-                                   _ptr(kv_cnt), _ptr(rl), _ptr(ws), ws.numel(), int(stages),
+                                   _ptr(kv_cnt), _ptr(rl), _ptr(ws), wsn, int(stages),
                                    _stream(q.device))
     _check("spa_build_mask", rc)
     return (kv_idx, kv_cnt, rl) if rule_len else (kv_idx, kv_cnt)
@@ -209,22 +242,29 @@ def sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, blk_q: int = 128, blk_k: int = 64,
     nqb, nkb = n_blocks(N, blk_q), n_blocks(N, blk_k)
     if tuple(kv_idx.shape) != (B, H, nqb, nkb) or tuple(kv_cnt.shape) != (B, H, nqb):
         raise ValueError("kv_idx / kv_cnt shapes do not match q and the block sizes")
+    for t, n in ((k, "k"), (v, "v"), (kv_idx, "kv_idx"), (kv_cnt, "kv_cnt")):
+        if t.device != q.device:
+            raise ValueError(f"{n} must be on {q.device}")
     if out is None:
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         o_lo = torch.empty_like(q) if with_residual else None
     else:
         o, lse, o_lo = out
+        _out_tensor(o, torch.bfloat16, q.shape, "o", q.device)
+        _out_tensor(lse, torch.float32, (B, H, N), "lse", q.device)
+        if with_residual and o_lo is None:
+            raise ValueError("with_residual=True needs an o_lo tensor in out")
+        if o_lo is not None:
+            _out_tensor(o_lo, torch.bfloat16, q.shape, "o_lo", q.device)
     dims = _dims(q.shape, blk_q, blk_k)
-    ws = None
+    ws, wsn = None, 0
     if o_lo is not None:
-        wsb = lib.spa_fwd_workspace_bytes(ctypes.byref(dims))
-        ws = workspace if workspace is not None else torch.empty(max(1, wsb), dtype=torch.uint8,
-                                                                device=q.device)
+        ws, wsn = _workspace(workspace, int(lib.spa_fwd_workspace_bytes(ctypes.byref(dims))),
+                             q.device, "workspace")
     rc = lib.spa_sparse_attn_fwd_stages(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
                                         _ptr(kv_idx), _ptr(kv_cnt), float(scale or 0.0), _ptr(o),
-                                        _ptr(o_lo), _ptr(lse), _ptr(ws),
-                                        ws.numel() if ws is not None else 0, int(stages),
+                                        _ptr(o_lo), _ptr(lse), _ptr(ws), wsn, int(stages),
                                         _stream(q.device))
     _check("spa_sparse_attn_fwd", rc)
     return (o, lse, o_lo) if with_residual else (o, lse)
@@ -235,7 +275,8 @@ def sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, blk_q: int = 128, blk_k
                     workspace=None, stages: int = BWD_ALL):
     """Block-sparse attention backward.  Returns (dq, dk, dv), fp32 unless grad_dtype=bf16.
 
-    Pass the forward's ``o_lo`` residual for full accuracy of D = <dO, O>.
+    Pass the forward's ``o_lo`` residual for full accuracy of D = <dO, O>.  Tensors given
+    in ``out`` must have the gradient dtype, the shape of q and be contiguous on q's device.
     """
     torch = _torch()
     lib = load_library()
@@ -259,17 +300,22 @@ def sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, blk_q: int = 128, blk_k
     gdt = torch.float32 if grad_dtype in (None, torch.float32) else grad_dtype
     if gdt not in (torch.float32, torch.bfloat16):
         raise ValueError("grad_dtype must be float32 or bfloat16")
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (do, "do"), (lse, "lse"), (kv_idx, "kv_idx"),
+                 (kv_cnt, "kv_cnt"), (o_lo, "o_lo")):
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{n} must be on {q.device}")
     if out is None:
         dq, dk, dv = (torch.empty(q.shape, dtype=gdt, device=q.device) for _ in range(3))
     else:
         dq, dk, dv = out
+        for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+            _out_tensor(t, gdt, q.shape, n, q.device)
     dims = _dims(q.shape, blk_q, blk_k)
-    wsb = lib.spa_bwd_workspace_bytes(ctypes.byref(dims))
-    ws = workspace if workspace is not None else torch.empty(max(1, wsb), dtype=torch.uint8,
-                                                            device=q.device)
+    ws, wsn = _workspace(workspace, int(lib.spa_bwd_workspace_bytes(ctypes.byref(dims))),
+                         q.device, "workspace")
     rc = lib.spa_sparse_attn_bwd_stages(
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(do), _ptr(lse),
         _ptr(kv_idx), _ptr(kv_cnt), float(scale or 0.0), _ptr(dq), _ptr(dk), _ptr(dv),
-        1 if gdt == torch.bfloat16 else 0, _ptr(ws), ws.numel(), int(stages), _stream(q.device))
+        1 if gdt == torch.bfloat16 else 0, _ptr(ws), wsn, int(stages), _stream(q.device))
     _check("spa_sparse_attn_bwd", rc)
     return dq, dk, dv

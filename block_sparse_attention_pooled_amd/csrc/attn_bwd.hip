@@ -119,8 +119,9 @@ struct DkdvSrc {
 };
 
 // Loads of stage st (64 query rows of query block qb) into one ring slot: the Q and dO
-// tiles and the lse2 / D rows (one 4-byte transfer per lane, waves 2 and 3).  Q and dO
-// rows at or beyond N read as zeros; their lse2 of +inf makes their P exactly 0.
+// tiles and the lse2 / D rows (one 4-byte transfer per lane, waves 2 and 3; the side
+// arrays are padded to whole query blocks).  Q and dO rows at or beyond N read as zeros;
+// their lse2 of +inf makes their P exactly 0.
 template <int D, int BQ>
 __device__ __forceinline__ void dkdv_load_stage(const DkdvSrc& src, int qb, int st, int w,
                                                 int lane, uint16_t* tq, float* sd) {
@@ -128,8 +129,8 @@ __device__ __forceinline__ void dkdv_load_stage(const DkdvSrc& src, int qb, int 
   const int row0 = qb * BQ + HR * (st % HPB);
   tile_load_lds_rsrc<D, HR, 8>(src.q, row0, tq);
   tile_load_lds_rsrc<D, HR, 8>(src.dout, row0, tq + HR * D);
-  if (w == 2) dma4(src.lse2, lane * 4, row0 * 4, lds_addr(sd));
-  if (w == 3) dma4(src.dsum, lane * 4, row0 * 4, lds_addr(sd + HR));
+  if (w == 2) dma4(rsrc_at(src.lse2, row0 * 4), lane * 4, lds_addr(sd));
+  if (w == 3) dma4(rsrc_at(src.dsum, row0 * 4), lane * 4, lds_addr(sd + HR));
 }
 
 // Both jobs issue their LDS reads in batches ahead of the MFMAs that consume them

@@ -8,9 +8,11 @@ so that the backward pass uses the same mask (the mask is held fixed: no gradien
 through the selection).  ``SpargeAttention`` is the ``nn.Module`` around it.
 
 Tensors are [B, H, N, d] on a ROCm device.  The kernels compute in bf16: other input
-dtypes (fp32 master activations, fp16) are rounded to bf16 on the way in; the output comes
-back in q's dtype and each gradient in its input's dtype.  Every step runs in the library's
-kernels; this file only marshals arguments.
+dtypes (fp32 master activations, fp16) are rounded to bf16 (nearest even) on the way in,
+and so is the incoming output gradient; the output comes back in q's dtype.  The kernels
+write the gradients in fp32, or directly in bf16 when every input is bf16; each gradient
+is returned in its input's dtype.  Every step runs in the library's kernels; this file only
+marshals arguments.
 """
 from __future__ import annotations
 
@@ -41,9 +43,12 @@ class SparseAttentionFunction(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, o, o_lo, lse, kv_idx, kv_cnt = ctx.saved_tensors
         blk_q, blk_k, scale = ctx.cfg
+        # fp32 gradients cost the kernels nothing extra: bf16 only when every input is bf16
+        gdt = (torch.bfloat16 if all(dt == torch.bfloat16 for dt in ctx.in_dtypes)
+               else torch.float32)
         dq, dk, dv = sparse_attn_bwd(q, k, v, o, do.contiguous().to(torch.bfloat16), lse,
                                      kv_idx, kv_cnt, blk_q, blk_k, scale, o_lo=o_lo,
-                                     grad_dtype=torch.bfloat16)
+                                     grad_dtype=gdt)
         dq, dk, dv = (g.to(dt) for g, dt in zip((dq, dk, dv), ctx.in_dtypes))
         return dq, dk, dv, None, None, None, None, None, None, None
 

@@ -167,20 +167,6 @@ def build_mask(q: np.ndarray, k: np.ndarray, blk_q: int, blk_k: int, k_frac: flo
     return out
 
 
-def mask_lists(mask: dict, B: int, H: int):
-    """Dense [B,H,Nqb,Nkb] int32 list array (ascending kept blocks, -1 padded) + counts."""
-    any_rows = next(iter(mask["rows"].values()))
-    nq = len(any_rows)
-    nk = any_rows[0]["order"].shape[0]
-    idx = np.full((B, H, nq, nk), -1, dtype=np.int32)
-    cnt = np.zeros((B, H, nq), dtype=np.int32)
-    for (b, h), rows in mask["rows"].items():
-        for i, r in enumerate(rows):
-            idx[b, h, i, :r["L"]] = r["keep"]
-            cnt[b, h, i] = r["L"]
-    return idx, cnt
-
-
 # ----------------------------------------------------------------------------------
 # O8: masked softmax attention over kept tiles ([P4] "Block-dünnbesetzte Aufmerksamkeit":
 # a tile is either kept whole or dropped; "Effiziente Kernel-Implementierung": dropped

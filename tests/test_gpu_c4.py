@@ -83,8 +83,9 @@ def test_c4_mask_sampled_heads(c4):
 
 def test_c4_fwd_and_dq_sampled(c4):
     h_, g = c4["host"], c4["g"]
-    for (b, hh, i) in _QBLOCKS:
-        log(f"[c4] fwd/dQ q-block (b={b}, h={hh}, i={i})")
+    heads = sorted({hh for (_, hh, _) in _QBLOCKS})
+    for (b, hh, i) in _QBLOCKS + parity.worst_qblocks(h_["kv_cnt"], heads):
+        log(f"[c4] fwd/dQ q-block (b={b}, h={hh}, i={i}), {h_['kv_cnt'][b, hh, i]} kept")
         lists = parity.lists_from_gpu(h_["kv_idx"][:, hh:hh + 1], h_["kv_cnt"][:, hh:hh + 1])
         f = {n: _head(g, n, hh) for n in ("q", "k", "v", "do")}
         o, lse = O.sparse_attn_fwd(f["q"], f["k"], f["v"], lists, W.blk_q, W.blk_k,
@@ -102,7 +103,8 @@ def test_c4_fwd_and_dq_sampled(c4):
 
 def test_c4_dkdv_sampled(c4):
     h_, g = c4["host"], c4["g"]
-    for (b, hh, j) in _KBLOCKS:
+    heads = sorted({hh for (_, hh, _) in _KBLOCKS})
+    for (b, hh, j) in _KBLOCKS + parity.worst_kblocks(h_["kv_idx"], h_["kv_cnt"], heads, W.n_kblk):
         lists = parity.lists_from_gpu(h_["kv_idx"][:, hh:hh + 1], h_["kv_cnt"][:, hh:hh + 1])
         users = [i for i, keep in enumerate(lists[(0, 0)]) if j in set(keep.tolist())]
         log(f"[c4] dK/dV key block (b={b}, h={hh}, j={j}) kept by {len(users)} query blocks")

@@ -11,6 +11,7 @@ with full attention, a student with the hybrid sparse module in every attention 
 import copy
 import sys
 
+import numpy as np
 import pytest
 import torch
 
@@ -156,3 +157,75 @@ def test_distill_steps_reduce_loss_and_leave_teacher(torch_gpu):
         assert torch.equal(p, t_before[n]), n
     changed = sum(not torch.equal(p, s_before[n]) for n, p in student.named_parameters())
     assert changed == len(s_before)
+
+
+class _Recorder(torch.nn.Module):
+    """Wraps an attention layer and keeps its inputs and output (with their gradients after
+    the backward pass) and the kept-block lists it used."""
+
+    def __init__(self, inner):
+        super().__init__()
+        self.inner = inner
+        self.inner.keep_mask = True
+        self.rec = None
+
+    def forward(self, q, k, v, mask=None):
+        for t in (q, k, v):
+            t.retain_grad()
+        o = self.inner(q, k, v, mask)
+        o.retain_grad()
+        self.rec = dict(q=q, k=k, v=v, o=o, mask=self.inner.last_mask)
+        return o
+
+
+@pytest.mark.parametrize("autocast", [False, True], ids=["fp32", "bf16_autocast"])
+def test_student_attention_layers_match_oracle(torch_gpu, autocast):
+    """Every sparse attention layer of the student, inside the distillation step: its output
+    and the gradients it hands back for its Q, K and V, element by element against the fp64
+    oracle on the layer's own inputs and output gradient (rounded to bf16 as the layer
+    rounds them), under the layer's own mask.  Without autocast the layer takes fp32
+    activations and returns fp32 gradients; under bf16 autocast it takes bf16.  The loss's
+    output gradient is ~1e-6, far below the absolute tolerance, and the gradients are linear
+    in it, so each gradient is compared after dividing both sides by the reference's
+    largest magnitude: the bounds then apply at unit scale and the relative bound always
+    applies."""
+    torch = torch_gpu
+    from block_sparse_attention_pooled_amd import distill as D
+    from oracle import spa_oracle as O
+    from tests import parity
+    teacher, student = D.make_pair(C_IN, DIM, HEADS, DEPTH, GRID, 0.10, 0.9)
+    recs = []
+    for blk in student.blocks:
+        blk.attn = _Recorder(blk.attn)
+        recs.append(blk.attn)
+    xt, t = _inputs(torch)
+    loss = D.velocity_distillation_loss(student, teacher, xt, t, autocast)
+    loss.backward()
+    torch.cuda.synchronize()
+
+    def bf16_f64(x):
+        b = x.detach().cpu().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        return O.widen_bf16(b)
+
+    for li, layer in enumerate(recs):
+        r = layer.rec
+        want_dt = torch.bfloat16 if autocast else torch.float32
+        assert r["q"].dtype == want_dt and r["q"].grad.dtype == want_dt
+        B, H, N, d = r["q"].shape
+        kv_idx, kv_cnt = r["mask"]
+        lists = parity.lists_from_gpu(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy())
+        f = {n: bf16_f64(r[n]) for n in ("q", "k", "v")}
+        f["do"] = bf16_f64(r["o"].grad)
+        ro, _ = O.sparse_attn_fwd(f["q"], f["k"], f["v"], lists, 128, 64)
+        rq, rk, rv = O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, 128, 64)
+        log(f"[distill layer {li} {'bf16' if autocast else 'fp32'}] shape {(B, H, N, d)} "
+            f"density {float(kv_cnt.float().mean()) / -(-N // 64):.3f} "
+            f"|dO|max {float(np.abs(f['do']).max()):.2e}")
+        for name, got, want in (("O", r["o"], ro), ("dQ", r["q"].grad, rq),
+                                ("dK", r["k"].grad, rk), ("dV", r["v"].grad, rv)):
+            gotn = got.detach().float().cpu().numpy().astype(np.float64)
+            s = 1.0 if name == "O" else float(np.abs(want).max())
+            assert s > 0.0, (li, name)
+            ok, mx, rel, _ = parity.close(gotn / s, want / s, vacuous=0.0)
+            log(f"  {name}: max_abs={mx:.3e} (after / {s:.2e}) rel_l2={rel:.3e}")
+            assert ok, (li, name, mx, rel)

@@ -72,11 +72,16 @@ def _sample_qblocks():
     return [(0, 0, 0), (0, 3, 97), (0, 7, 200), (0, 11, W.n_qblk - 1), (0, 5, 128)]
 
 
+def _sample_kblocks():
+    return [(0, 0, 0), (0, 4, 255), (0, 11, W.n_kblk - 1), (0, 8, 301)]
+
+
 def test_fullsize_fwd_and_dq_sampled(c2):
     h, f = c2["host"], c2["f64"]
     lists = parity.lists_from_gpu(h["kv_idx"], h["kv_cnt"])
-    for (b, hh, i) in _sample_qblocks():
-        log(f"[fullsize] fwd/dQ q-block (b={b}, h={hh}, i={i})")
+    heads = sorted({hh for (_, hh, _) in _sample_qblocks()})
+    for (b, hh, i) in _sample_qblocks() + parity.worst_qblocks(h["kv_cnt"], heads):
+        log(f"[fullsize] fwd/dQ q-block (b={b}, h={hh}, i={i}), {h['kv_cnt'][b, hh, i]} kept")
         o, lse = O.sparse_attn_fwd(f["q"], f["k"], f["v"], lists, W.blk_q, W.blk_k,
                                    heads=[(b, hh)], qblocks=[i])
         s, e = i * W.blk_q, min(W.N, (i + 1) * W.blk_q)
@@ -95,7 +100,9 @@ def test_fullsize_fwd_and_dq_sampled(c2):
 def test_fullsize_dkdv_sampled(c2):
     h, f = c2["host"], c2["f64"]
     lists = parity.lists_from_gpu(h["kv_idx"], h["kv_cnt"])
-    for (b, hh, j) in [(0, 0, 0), (0, 4, 255), (0, 11, W.n_kblk - 1), (0, 8, 301)]:
+    heads = sorted({hh for (_, hh, _) in _sample_kblocks()})
+    for (b, hh, j) in _sample_kblocks() + parity.worst_kblocks(h["kv_idx"], h["kv_cnt"], heads,
+                                                        W.n_kblk):
         users = [i for i, keep in enumerate(lists[(b, hh)]) if j in set(keep.tolist())]
         log(f"[fullsize] dK/dV key block (b={b}, h={hh}, j={j}) kept by {len(users)} query blocks")
         _, dk, dv = O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, W.blk_q, W.blk_k,

@@ -179,3 +179,26 @@ def test_bf16_gradients_are_rounded_fp32_gradients(torch_gpu, wname):
     for name, a, b in zip(("dQ", "dK", "dV"), g32, g16):
         assert a.dtype == torch.float32 and b.dtype == torch.bfloat16
         assert torch.equal(a.to(torch.bfloat16), b), name
+
+
+@pytest.mark.parametrize("blk_q", [128, 64])
+def test_mask_d128_at_2048_key_blocks(torch_gpu, blk_q):
+    """The mask at d = 128 with 2048 key blocks (N = 131040, ragged: last key block 32 keys),
+    where the selection kernel's pooled-logit rows take its whole 160 KiB of LDS: every row
+    against the oracle."""
+    torch = torch_gpu
+    w = synth.Workload("max_d128", 1, 1, 131040, 128, blk_q, 64, 0.05, 0.9, kind="video",
+                       grid=(9, 112, 130), alpha=synth.ALPHA_480P, n_sinks=4, seed=13)
+    assert w.n_kblk == 2048
+    log(f"[limits mask d128 blk_q={blk_q}] shape={w.shape()}")
+    g = synth.generate(w, with_do=False)
+    q, k = (torch.from_numpy(g[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k"))
+    kv_idx, kv_cnt, rl = spa.build_mask(q, k, w.blk_q, w.blk_k, w.k_frac, w.p, rule_len=True)
+    torch.cuda.synchronize()
+    idx, cnt, rl = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), rl.cpu().numpy()
+    f = {n: O.widen_bf16(g[n]) for n in ("q", "k")}
+    mask = O.build_mask(f["q"], f["k"], w.blk_q, w.blk_k, w.k_frac, w.p)
+    n, exempt, fails = parity.compare_mask_rows(idx, cnt, mask["rows"], w.p)
+    log(f"  {n} rows, {len(exempt)} exempt, mean kept {cnt.mean():.1f} of {w.n_kblk}")
+    assert n == w.n_qblk and not fails, fails[:5]
+    assert np.all(rl[..., 0] == O.topk_count(w.k_frac, w.n_kblk))

@@ -397,3 +397,51 @@ def test_determinism(torch_gpu):
     for key in a:
         if key != "kv_idx":
             assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+NAN_GUARD_CASES = [("n1000_d128_q128", small_workload(1000, 128, 128, grid=(2, 20, 25))),
+                   ("n777_d64_q64", small_workload(777, 64, 64, grid=(3, 7, 37))),
+                   ("n1000_d128_q64", small_workload(1000, 128, 64, grid=(2, 20, 25)))]
+
+
+def _front_of_nan_buffer(torch, bits, pad_rows=128):
+    """A contiguous device bf16 tensor holding `bits`, placed at the front of a larger
+    allocation whose remaining pad_rows rows hold NaN."""
+    shape, d = bits.shape, bits.shape[-1]
+    buf = torch.full((bits.size + pad_rows * d,), float("nan"), dtype=torch.bfloat16,
+                     device="cuda")
+    buf[:bits.size].copy_(to_dev(torch, bits).reshape(-1))
+    return buf[:bits.size].view(shape)
+
+
+@pytest.mark.parametrize("tag,w", NAN_GUARD_CASES, ids=[c[0] for c in NAN_GUARD_CASES])
+def test_rows_beyond_n_are_never_read(torch_gpu, tag, w):
+    """Partial last blocks stage rows at or beyond N as zeros through the buffer range
+    check, never from the memory after the tensor: Q, K, V and dO are views at the front of
+    NaN-filled allocations (so rows past the last head's end are NaN), the workspaces are
+    filled with NaN bit patterns, and every output must be finite and match the oracle."""
+    torch = torch_gpu
+    log(f"[case nan guard {tag}] shape={w.shape()} blk=({w.blk_q},{w.blk_k})")
+    g = synth.generate(w)
+    q, k, v, do = (_front_of_nan_buffer(torch, g[n]) for n in ("q", "k", "v", "do"))
+    kv_idx, kv_cnt = spa.build_mask(q, k, w.blk_q, w.blk_k, w.k_frac, w.p)
+    fws = torch.full((spa.fwd_workspace_bytes(q.shape, w.blk_q, w.blk_k),), 255,
+                     dtype=torch.uint8, device=q.device)
+    bws = torch.full((spa.bwd_workspace_bytes(q.shape, w.blk_q, w.blk_k),), 255,
+                     dtype=torch.uint8, device=q.device)
+    o, lse, o_lo = spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                                       with_residual=True, workspace=fws)
+    o_plain, _ = spa.sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, w.blk_q, w.blk_k)
+    dq, dk, dv = spa.sparse_attn_bwd(q, k, v, o, do, lse, kv_idx, kv_cnt, w.blk_q, w.blk_k,
+                                     o_lo=o_lo, workspace=bws)
+    torch.cuda.synchronize()
+    got = {"O": o, "O without residual": o_plain, "LSE": lse, "dQ": dq, "dK": dk, "dV": dv}
+    for name, t in got.items():
+        assert bool(torch.isfinite(t.float()).all()), f"{name} has non-finite values"
+    f = {n: O.widen_bf16(g[n]) for n in ("q", "k", "v", "do")}
+    lists = parity.lists_from_gpu(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy())
+    ro, rl = O.sparse_attn_fwd(f["q"], f["k"], f["v"], lists, w.blk_q, w.blk_k)
+    rq, rk, rv = O.sparse_attn_bwd(f["q"], f["k"], f["v"], f["do"], lists, w.blk_q, w.blk_k)
+    for name, want in (("O", ro), ("O without residual", ro), ("LSE", rl), ("dQ", rq),
+                       ("dK", rk), ("dV", rv)):
+        check_close(name, got[name].float().cpu().numpy(), want)

@@ -85,7 +85,8 @@ def test_stress_attention_sampled(st):
                                      kv_cnt, W.blk_q, W.blk_k, o_lo=o_lo)
     torch.cuda.synchronize()
     idx, cnt = kv_idx.cpu().numpy(), kv_cnt.cpu().numpy()
-    for hh, i in ((2, 77), (8, 200)):
+    extra_q = [(hh, i) for (_, hh, i) in parity.worst_qblocks(cnt, (2, 8))]
+    for hh, i in [(2, 77), (8, 200)] + extra_q:
         log(f"[stress] fwd/dQ head {hh} q-block {i} ({cnt[0, hh, i]} kept blocks)")
         lists = parity.lists_from_gpu(idx[:, hh:hh + 1], cnt[:, hh:hh + 1])
         f = {n: _head(st, n, hh) for n in ("q", "k", "v", "do")}
@@ -100,7 +101,8 @@ def test_stress_attention_sampled(st):
             ok, mx, rel, _ = parity.close(got, want)
             log(f"  {name}: max_abs={mx:.3e} rel_l2={rel:.3e}")
             assert ok, (name, mx, rel)
-    for hh, j in ((9, 0), (3, 311)):
+    extra_k = [(hh, j) for (_, hh, j) in parity.worst_kblocks(idx, cnt, (9, 3), W.n_kblk)]
+    for hh, j in [(9, 0), (3, 311)] + extra_k:
         lists = parity.lists_from_gpu(idx[:, hh:hh + 1], cnt[:, hh:hh + 1])
         users = [i for i, keep in enumerate(lists[(0, 0)]) if j in set(keep.tolist())]
         log(f"[stress] dK/dV head {hh} key block {j}, kept by {len(users)} query blocks")

@@ -15,6 +15,29 @@ from oracle import spa_oracle as O
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
+# ------------------------------------------------------------------ input widening
+def test_widen_bf16_matches_torch_on_every_bit_pattern():
+    # all 65536 bf16 patterns: normals, subnormals, both zeros, both infinities, NaNs
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.widen_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2 * 127  # exponent all ones with a nonzero 7-bit fraction, two signs
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))  # -0 stays -0
+
+
+def test_widen_bf16_closed_forms():
+    # 0x3F80 = 1.0, 0xC000 = -2.0, 0x0001 = 2^-133 (smallest subnormal), 0x7F7F = largest
+    # finite (2 - 2^-7) 2^127, 0x7F80 = +inf, 0x8000 = -0
+    bits = np.array([0x3F80, 0xC000, 0x0001, 0x7F7F, 0x7F80, 0x8000], dtype=np.uint16)
+    got = O.widen_bf16(bits)
+    assert got[0] == 1.0 and got[1] == -2.0 and got[2] == 2.0 ** -133
+    assert got[3] == (2.0 - 2.0 ** -7) * 2.0 ** 127 and got[4] == np.inf
+    assert got[5] == 0.0 and np.signbit(got[5])
+
+
 # ------------------------------------------------------------------ pooling (O1, O2)
 def test_pool_closed_form_with_partial_tail():
     # Q[t] = t * ones: the block mean is the block centre; the tail block [96, 100)

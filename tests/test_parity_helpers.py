@@ -14,6 +14,25 @@ def test_close_applies_both_bounds():
     assert not ok and mx > 2e-2
 
 
+def test_close_rejects_a_zero_output_below_the_absolute_tolerance():
+    # a reference slice of size ~1e-2 (inside the max-abs bound everywhere): an all-zero
+    # output meets max-abs 2e-2 but must fail on relative L2
+    want = np.random.default_rng(0).uniform(-1e-2, 1e-2, 4096)
+    ok, mx, rel, _ = parity.close(np.zeros_like(want), want)
+    assert mx <= 2e-2 and rel == 1.0 and not ok
+    ok, _, _, _ = parity.close(want * 1.005, want)     # 0.5 % relative error passes
+    assert ok
+    want = np.full(64, 5e-6)                            # above the vacuity level
+    assert not parity.close(np.zeros_like(want), want)[0]
+
+
+def test_close_rejects_non_finite_output():
+    want = np.linspace(-1.0, 1.0, 64)
+    got = want.copy()
+    got[3] = np.nan
+    assert not parity.close(got, want)[0]
+
+
 def test_close_vanishing_reference_uses_max_abs_only():
     want = np.full(512, 1e-22)                           # a gradient that is zero in effect
     ok, _, rel, _ = parity.close(want + 1e-4, want)
