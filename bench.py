@@ -31,6 +31,10 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd+bwd ms/layer & MFMA util at 95% block sparsity, N=32760 H=12 d=128"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PRECISION = ("bf16 Q/K/V/dO; fp32 accumulation, softmax and gradients; S and dP as bf16 "
+             "products; P*V and dV = P^T dO as fp16 products of P (one rounding) against "
+             "range-checked fp16 copies of V and dO (a bf16 hi+lo pair of P where a block is "
+             "not eligible); dS as a bf16 hi+lo pair (two products); mask in fp64")
 
 
 def log(msg):
@@ -51,18 +55,39 @@ def kept_pairs_weight(kv_idx, kv_cnt, N, bq, bk):
     return total
 
 
-def cpu_oracle_baseline(g, w, lists, budget_s: float):
+def host_cpu_info():
+    """CPU model and counts of the host this process runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "host_logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def cpu_oracle_baseline(g, w, lists, budget_s: float, single_budget_s: float):
     """Time the CPU oracle on a bounded sample of the layer and scale to ms/layer.
 
     The mask is computed for every head; forward + backward run query block by query
     block (all heads, a fixed interleaved order) until the time budget is spent, and the
-    per-block time is scaled to the whole layer.
+    per-block time is scaled to the whole layer.  Then the same on one head with the BLAS
+    thread pool limited to one thread (query blocks of head 0 until `single_budget_s` is
+    spent, scaled to the head).
     """
     from oracle import spa_oracle as O
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count()
     f = {n: O.widen_bf16(g[n]) for n in ("q", "k", "v", "do")}
     t0 = time.perf_counter()
@@ -71,25 +96,43 @@ def cpu_oracle_baseline(g, w, lists, budget_s: float):
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     order = [(heads[x % len(heads)], (x * 37) % w.n_qblk)
              for x in range(len(heads) * w.n_qblk)]
-    done = 0
-    t0 = time.perf_counter()
-    for ((b, h), i) in order:
-        one = {n: f[n][b:b + 1, h:h + 1] for n in f}   # this head only
-        l1 = {(0, 0): lists[(b, h)]}
-        O.sparse_attn_fwd(one["q"], one["k"], one["v"], l1, w.blk_q, w.blk_k, qblocks=[i])
-        O.sparse_attn_bwd(one["q"], one["k"], one["v"], one["do"], l1, w.blk_q, w.blk_k,
-                          qblocks=[i])
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    t_attn = time.perf_counter() - t0
+
+    def run_units(units, budget):
+        done = 0
+        t0 = time.perf_counter()
+        for ((b, h), i) in units:
+            one = {n: f[n][b:b + 1, h:h + 1] for n in f}   # this head only
+            l1 = {(0, 0): lists[(b, h)]}
+            O.sparse_attn_fwd(one["q"], one["k"], one["v"], l1, w.blk_q, w.blk_k, qblocks=[i])
+            O.sparse_attn_bwd(one["q"], one["k"], one["v"], one["do"], l1, w.blk_q, w.blk_k,
+                              qblocks=[i])
+            done += 1
+            if time.perf_counter() - t0 > budget:
+                break
+        return done, time.perf_counter() - t0
+
+    done, t_attn = run_units(order, budget_s)
     per_layer = t_mask + t_attn / done * len(order)
-    return {
+    out = {
         "value": per_layer * 1e3, "unit": "ms/layer", "cores": int(threads), "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: mask of all {len(heads)} heads ({t_mask:.2f} s) and "
-                   f"fwd+bwd of {done} of {len(order)} (head, query block) units "
-                   f"({t_attn:.2f} s), scaled linearly to the whole layer"),
+        "sample": (f"fp64 numpy oracle on {threads} BLAS threads: mask of all {len(heads)} heads "
+                   f"({t_mask:.2f} s) and fwd+bwd of {done} of {len(order)} (head, query block) "
+                   f"units ({t_attn:.2f} s), scaled linearly to the whole layer"),
     }
+    out.update(host_cpu_info())
+    if threadpool_limits is not None and single_budget_s > 0:
+        with threadpool_limits(limits=1):
+            h0 = {n: f[n][:1, :1] for n in f}
+            t0 = time.perf_counter()
+            O.build_mask(h0["q"], h0["k"], w.blk_q, w.blk_k, w.k_frac, w.p)
+            t_mask1 = time.perf_counter() - t0
+            units = [((0, 0), (x * 37) % w.n_qblk) for x in range(w.n_qblk)]
+            done1, t1 = run_units(units, single_budget_s)
+        out["single_thread_one_head_ms"] = (t_mask1 + t1 / done1 * w.n_qblk) * 1e3
+        out["single_thread_sample"] = (f"head 0 with one BLAS thread: mask ({t_mask1:.2f} s) and "
+                                       f"fwd+bwd of {done1} of {w.n_qblk} query blocks "
+                                       f"({t1:.2f} s), scaled to the head")
+    return out
 
 
 def main():
@@ -101,6 +144,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work to time for the baseline")
+    ap.add_argument("--cpu-single-budget", type=float, default=6.0,
+                    help="seconds of single-thread oracle work on one head")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps timed with the 256 MB last-level cache flushed before "
@@ -240,15 +285,27 @@ def main():
                + stage_ms["bwd_dkdv"] + stage_ms["bwd_dq"])
     mask_in_step_ms = stage_ms["mask_pool"] + stage_ms["mask_select"]
     # the mask kernels alone (pool + select back to back, nothing on the second stream):
-    # inside a step the selection shares the GPU with the forward's preparation
-    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for s_ in range(args.steps):
-        mev[s_][0].record(stream)
-        spa.build_mask(q, k, w.blk_q, w.blk_k, w.k_frac, w.p, out=(kv_idx, kv_cnt, None),
-                       workspace=mws)
-        mev[s_][1].record(stream)
-    torch.cuda.synchronize()
-    mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in mev]))
+    # inside a step the selection shares the GPU with the forward's preparation.  The
+    # headline figure reads Q and K from HBM: reading 512 MB before each timed call evicts
+    # them from the 256 MB last-level cache (which holds both at this shape); the warm
+    # figure (back-to-back calls, Q and K largely cache-resident) is reported beside it.
+    def time_mask(flush_buf):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for s_ in range(args.steps):
+            if flush_buf is not None:
+                float(flush_buf.sum())
+                torch.cuda.synchronize()
+            evs[s_][0].record(stream)
+            spa.build_mask(q, k, w.blk_q, w.blk_k, w.k_frac, w.p, out=(kv_idx, kv_cnt, None),
+                           workspace=mws)
+            evs[s_][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+    mask_ms_warm = time_mask(None)
+    flush = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+    mask_ms = time_mask(flush)
+    del flush
 
     # ---- cold-cache steps: reading 512 MB evicts the 256 MB last-level cache before each
     # step (a read, so that no dirty lines are written back during the step) -------------
@@ -318,7 +375,7 @@ def main():
         log("[bench] timing the CPU oracle on a sample")
         lists = {(b, h): [idx_h[b, h, i, :cnt_h[b, h, i]].astype(np.int64) for i in range(nqb)]
                  for b in range(B) for h in range(H)}
-        cpu = cpu_oracle_baseline(g, w, lists, args.cpu_budget)
+        cpu = cpu_oracle_baseline(g, w, lists, args.cpu_budget, args.cpu_single_budget)
         log(f"[bench] cpu oracle: {cpu['value']:.1f} ms/layer on {cpu['cores']} threads")
     out = {
         "metric": METRIC, "value": ms_per_step, "unit": "ms/layer", "n_gpus": 1,
@@ -328,12 +385,14 @@ def main():
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "blk_q": w.blk_q,
                    "blk_k": w.blk_k, "k_frac": w.k_frac, "p": w.p, "alpha": w.alpha,
                    "grid": list(w.grid) if w.grid else None, "density": density,
-                   "grad_dtype": "fp32"},
+                   "grad_dtype": "fp32", "precision": PRECISION},
         "stage_ms": stage_ms, "mask_ms": mask_ms, "mask_in_step_ms": mask_in_step_ms,
         "attn_fwd_bwd_ms": attn_ms,
         "credited_tflops_fwd_bwd": fl_total / (attn_ms * 1e-3) / 1e12,
         "mfma_util_credited": fl_total / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "mask_hbm_frac": mask_bytes / (mask_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "mask_ms_warm": mask_ms_warm,
+        "mask_hbm_frac_warm_cache": mask_bytes / (mask_ms_warm * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "rules": rules, "cold_cache": cold,
         "roofline": roofline, "dense": dense, "cpu_baseline": cpu,
     }

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline():
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny_sparse",
            "--steps", "3", "--warmup", "1", "--dense-steps", "1", "--cold-steps", "1",
-           "--cpu-budget", "1"]
+           "--cpu-budget", "1", "--cpu-single-budget", "0.5"]
     print("bench:", " ".join(cmd[1:]), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-3000:]
@@ -42,3 +42,9 @@ def test_bench_prints_one_json_line_with_roofline_and_cpu_baseline():
     cb = rep["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
     assert cb["unit"] == rep["unit"] and cb["sample"]
+    assert cb["host_logical_cpus"] >= 1 and cb["usable_cpus"] >= 1
+    assert cb["single_thread_one_head_ms"] > 0 and cb["single_thread_sample"]
+    # the mask's headline rate is the cold-cache one; the warm figure is labelled apart
+    assert rep["mask_ms"] > 0 and rep["mask_ms_warm"] > 0
+    assert 0 < rep["mask_hbm_frac"] < 1 and 0 < rep["mask_hbm_frac_warm_cache"]
+    assert "fp16" in rep["config"]["precision"]
