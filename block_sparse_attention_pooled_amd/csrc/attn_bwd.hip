@@ -124,13 +124,14 @@ struct DkdvSrc {
 // their lse2 of +inf makes their P exactly 0.
 template <int D, int BQ>
 __device__ __forceinline__ void dkdv_load_stage(const DkdvSrc& src, int qb, int st, int w,
-                                                int lane, uint16_t* tq, float* sd) {
+                                                int lane, uint16_t* tq, float* sd,
+                                                const TileLanes<D, 64, 8>& tl) {
   constexpr int HR = 64, HPB = BQ / HR;
   const int row0 = qb * BQ + HR * (st % HPB);
-  tile_load_lds_rsrc<D, HR, 8>(src.q, row0, tq);
-  tile_load_lds_rsrc<D, HR, 8>(src.dout, row0, tq + HR * D);
-  if (w == 2) dma4(rsrc_at(src.lse2, row0 * 4), lane * 4, lds_addr(sd));
-  if (w == 3) dma4(rsrc_at(src.dsum, row0 * 4), lane * 4, lds_addr(sd + HR));
+  tile_load_lds_rsrc<D, HR, 8>(src.q, row0, tq, tl);
+  tile_load_lds_rsrc<D, HR, 8>(src.dout, row0, tq + HR * D, tl);
+  if (w == 2) dma4(src.lse2, lane * 4, row0 * 4, lds_addr(sd));
+  if (w == 3) dma4(src.dsum, lane * 4, row0 * 4, lds_addr(sd + HR));
 }
 
 // Both jobs issue their LDS reads in batches ahead of the MFMAs that consume them
@@ -341,6 +342,7 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   src.lse2 = make_rsrc(lse2p + (size_t)bh * npad, (uint32_t)npad * 4);
   src.dsum = make_rsrc(dsum + (size_t)bh * npad, (uint32_t)npad * 4);
   for (int x = threadIdx.x; x < cnt; x += 512) lst[x] = list[x];
+  const TileLanes<D, 64, 8> tl;
   __syncthreads();
   auto list_at = [&](int st) {
     return __builtin_amdgcn_readfirstlane(lst[max(0, min(st / HPB, cnt - 1))]);
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   uint32_t rbits = 0;  // bit 3: a listed dO block is flagged; bits 0-2: V range classes
   for (int x = threadIdx.x; x < cnt; x += 512)
     rbits |= doflag[(size_t)bh * nqb + lst[x]] != 0 ? 8u : 0u;
-  if (nst > 0) dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tiles[0], side[0]);
+  if (nst > 0) dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tiles[0], side[0], tl);
 
   bf16x8 bf[KS];  // producer: K row of this lane's key; consumer: V row
   {
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   const bool use16 = !(all & 8u) && f16_block_ok(all & 7u);
   if (!use16) {  // stage 0 again, from bf16 dO
     src.dout = make_rsrc(dout + head, (uint32_t)N * D * 2);
-    if (nst > 0) dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tiles[0], side[0]);
+    if (nst > 0) dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tiles[0], side[0], tl);
     wait_vmem();
     __syncthreads();
   }
@@ -389,7 +391,7 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
     int qn = list_at(1);                                                                   \
     for (int st = 0; st <= nst; ++st) {                                                    \
       const int nxt = cur == 2 ? 0 : cur + 1;                                              \
-      if (st + 1 < nst) dkdv_load_stage<D, BQ>(src, qn, st + 1, w, lane, tiles[nxt], side[nxt]); \
+      if (st + 1 < nst) dkdv_load_stage<D, BQ>(src, qn, st + 1, w, lane, tiles[nxt], side[nxt], tl); \
       const int qn_v = lst[max(0, min((st + 2) / HPB, cnt - 1))];                           \
       __VA_ARGS__;                                                                         \
       wait_vmem();                                                                         \
@@ -609,6 +611,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   // the lists are trusted; the clamp only keeps a corrupt count inside the LDS list
   const int cnt = min(max(kv_cnt[(size_t)bh * nqb + i], 0), nkb);
   for (int x = threadIdx.x; x < cnt; x += NT) lst[x] = list[x];
+  const TileLanes<D, kBlkK, NT / 64> tl;
   auto blk = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[min(t, cnt - 1)]); };
 
   const int qrow = i * BQ + 32 * wv + c;
@@ -655,8 +658,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   }
   if (cnt > 0) {
     const int j0 = blk(0);
-    tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0]);
-    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, j0 * kBlkK, smem[0][1]);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0], tl);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, j0 * kBlkK, smem[0][1], tl);
   }
   wait_vmem();  // also the row fragments: nothing vector-memory is pending inside the loop
   __syncthreads();
@@ -670,8 +673,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   for (int t = 0; t < cnt_main; ++t) {
     const int buf = t & 1;
     if (t + 1 < cnt) {  // the next tile streams into the other buffer meanwhile
-      tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0]);
-      tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, jn * kBlkK, smem[buf ^ 1][1]);
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0], tl);
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, jn * kBlkK, smem[buf ^ 1][1], tl);
     }
     const int jn_v = lst[min(t + 2, cnt - 1)];
     dq_tile<D, false>(smem[buf][0], smem[buf][1], 0 /* read by the tail form only */, N, qf,

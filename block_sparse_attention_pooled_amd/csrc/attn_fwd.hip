@@ -219,13 +219,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  const TileLanes<D, kBlkK, NT / 64> tl;
   __syncthreads();  // list staged
   auto blk = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[min(t, cnt - 1)]); };
   const u32x4 vsrc = use16 ? v16rs : vrs;
   if (cnt > 0) {
     const int j0 = blk(0);
-    tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0]);
-    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vsrc, j0 * kBlkK, smem[0][1]);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0], tl);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vsrc, j0 * kBlkK, smem[0][1], tl);
   }
   wait_vmem();  // also the Q fragments: nothing vector-memory is pending inside the loop
   __syncthreads();
@@ -239,8 +240,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
     for (int t = 0; t < cnt_main; ++t) {                                                   \
       const int buf = t & 1;                                                               \
       if (t + 1 < cnt) {                                                                   \
-        tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0]);          \
-        tile_load_lds_rsrc<D, kBlkK, NT / 64>(vsrc, jn * kBlkK, smem[buf ^ 1][1]);         \
+        tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0], tl);      \
+        tile_load_lds_rsrc<D, kBlkK, NT / 64>(vsrc, jn * kBlkK, smem[buf ^ 1][1], tl);     \
       }                                                                                    \
       const int jn_v = lst[min(t + 2, cnt - 1)];                                           \
       /* key0 is read by the tail form only */                                            \

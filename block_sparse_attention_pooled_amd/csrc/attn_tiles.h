@@ -42,29 +42,33 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
-// The resource r rebased at byte `off` of its range.  The range check of a raw buffer
-// load compares the per-lane (VGPR) offset with the record count; the scalar offset is
-// added after the check and never compared.  A tile that starts at a row offset must
-// therefore move the base (and shorten the range) for rows at or beyond the end of the
-// buffer to read as zeros.  Past the end, the range is empty and every load reads zeros.
-__device__ __forceinline__ u32x4 rsrc_at(const u32x4& r, uint32_t off) {
-  const uint64_t b = ((((uint64_t)(r.y & 0xFFFFu)) << 32) | r.x) + off;
-  u32x4 o;
-  o.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  o.y = __builtin_amdgcn_readfirstlane((r.y & 0xFFFF0000u) | ((uint32_t)(b >> 32) & 0xFFFFu));
-  o.z = __builtin_amdgcn_readfirstlane(off < r.z ? r.z - off : 0u);
-  o.w = __builtin_amdgcn_readfirstlane(r.w);
-  return o;
-}
-
 // One buffer->LDS transfer of 16 bytes per lane: lane l's bytes land at LDS byte address
-// lds_addr + 16*l, read from byte voff of the resource (the scalar offset is 0, so the
-// whole address is range-checked).  Issued as inline assembly so that the compiler's
+// lds_addr + 16*l, read from byte soff + voff of the resource.  The range check of a raw
+// buffer load compares only the per-lane (VGPR) offset with the record count: the scalar
+// offset soff is added after the check, so it may carry an offset only where every byte of
+// the transfer is known to be in range.  Issued as inline assembly so that the compiler's
 // wait-count tracking does not see it: it would otherwise make every LDS read wait for all
 // transfers still in flight (it cannot tell which buffer they target), exposing the load
 // latency each step.  The caller waits (wait_vmem) and synchronises before reading the
 // data.  M0 is restored.
-__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t soff,
+                                      uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
+      : "memory");
+}
+
+// The same with the scalar offset 0: the whole offset is range-checked, so bytes at or
+// beyond the end of the resource read as zeros.
+__device__ __forceinline__ void dma16_checked(const u32x4& rsrc, uint32_t voff,
+                                              uint32_t lds_addr) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -77,17 +81,19 @@ __device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t voff, uint32_t
       : "memory");
 }
 
-// The same with 4 bytes per lane (lane l's word at lds_addr + 4*l).
-__device__ __forceinline__ void dma4(const u32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+// 4 bytes per lane (lane l's word at lds_addr + 4*l), from byte soff + voff; the same rule
+// for soff as dma16.
+__device__ __forceinline__ void dma4(const u32x4& rsrc, uint32_t voff, uint32_t soff,
+                                     uint32_t lds_addr) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %4\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dword %1, %2, 0 offen lds\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
       : "memory");
 }
 
@@ -95,25 +101,42 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
-// Tile staging through a buffer resource over one head's [N, D] matrix: the resource is
-// rebased at the tile's first row (rsrc_at), so the per-lane offsets are loop invariant
-// and rows at or beyond N read as zeros (the range check of the resource).
+// Per-lane byte offsets of a tile transfer within its tile (row-major [NROWS, D] bf16 in
+// HBM; the LDS side is the swizzled Tile layout), computed once per workgroup.  The empty
+// asm statements make the values opaque, so that the compiler keeps them in registers
+// across the staging loops instead of recomputing them before every transfer.
 template <int D, int NROWS, int NWAVES>
-__device__ __forceinline__ void tile_load_lds_rsrc(const u32x4& rsrc, int row0, uint16_t* lds) {
-  constexpr int SEGS = NROWS * D * 2 / 1024;
-  constexpr int PER = SEGS / NWAVES;
-  constexpr int RPS = 1024 / (D * 2);
+struct TileLanes {
+  static constexpr int SEGS = NROWS * D * 2 / 1024;
+  static constexpr int PER = SEGS / NWAVES;
+  static constexpr int RPS = 1024 / (D * 2);
   static_assert(SEGS % NWAVES == 0, "segments must divide among the waves");
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const u32x4 rs = rsrc_at(rsrc, (uint32_t)row0 * D * 2);
+  uint32_t off[PER];
+  __device__ __forceinline__ TileLanes() {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int seg = wv * PER + u;
-    const int row = seg * RPS + lane / Tile<D>::CPR;
-    const int cc = (lane % Tile<D>::CPR) ^ Tile<D>::swz(row);
-    dma16(rs, (uint32_t)(row * D + cc * 8) * 2, lds_addr(lds + seg * 512));
+    for (int u = 0; u < PER; ++u) {
+      const int row = (wv * PER + u) * RPS + lane / Tile<D>::CPR;
+      const int cc = (lane % Tile<D>::CPR) ^ Tile<D>::swz(row);
+      off[u] = (uint32_t)(row * D + cc * 8) * 2;
+      asm volatile("" : "+v"(off[u]));
+    }
   }
+};
+
+// Tile staging through a buffer resource over one head's [N, D] matrix: the tile's first
+// row is added to the per-lane offsets, so the range check of the resource sees every
+// byte offset and rows at or beyond N read as zeros.
+template <int D, int NROWS, int NWAVES>
+__device__ __forceinline__ void tile_load_lds_rsrc(const u32x4& rsrc, int row0, uint16_t* lds,
+                                                   const TileLanes<D, NROWS, NWAVES>& tl) {
+  constexpr int PER = TileLanes<D, NROWS, NWAVES>::PER;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t base = (uint32_t)row0 * D * 2;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    dma16_checked(rsrc, base + tl.off[u], lds_addr(lds + (wv * PER + u) * 512));
 }
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone), issued through the builtin so that
