@@ -69,10 +69,20 @@ __global__ __launch_bounds__(256) void k_vconv(const uint16_t* __restrict__ v,
 template <int D, bool SPLIT, bool TAIL, bool V16>
 __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs, int key0, int N,
                                          const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
-                                         float& m_run, float& l_run, float scale_log2, int lane) {
+                                         float& m_run, float& l_run, float scale_log2, int lane,
+                                         const ColFragLanes<D>& cf) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   const int h = lane >> 5;
+  // per-lane LDS byte addresses of this V tile's transpose reads (k-step 0; the other
+  // k-steps are immediate offsets from them)
+  uint32_t vlo[DB], vhi[DB];
+  const uint32_t vbase = lds_addr(Vs);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    vlo[db] = vbase + cf.off[db][0];
+    vhi[db] = vbase + cf.off[db][1];
+  }
   // ---- S^T = K Q^T : two 32-key slabs, K fragments read in batches of four k-steps ------
   f32x16 sc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -107,7 +117,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) va0[kk][db] = lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
+    for (int db = 0; db < DB; ++db) va0[kk][db] = lds_colfrag_at<D>(vlo[db], vhi[db], kk);
   SPA_FENCE();
   // ---- online softmax (log2 domain, scale folded into the exponent) --------------------
   float mloc = sc[0][0];
@@ -144,7 +154,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
       const f16x8 ph = to_f16x8(sc[kk >> 1], kk & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 va = kk < 2 ? va0[kk][db] : lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
+        const bf16x8 va = kk < 2 ? va0[kk][db] : lds_colfrag_at<D>(vlo[db], vhi[db], kk);
         oacc[db] = mfma32h(__builtin_bit_cast(f16x8, va), ph, oacc[db]);
       }
     }
@@ -158,7 +168,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
         ph = to_bf16x8(sc[kk >> 1], kk & 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 va = kk < 2 ? va0[kk][db] : lds_colfrag<D>(Vs, 16 * kk, 32 * db, lane);
+        const bf16x8 va = kk < 2 ? va0[kk][db] : lds_colfrag_at<D>(vlo[db], vhi[db], kk);
         oacc[db] = mfma32(va, ph, oacc[db]);
         if constexpr (SPLIT) oacc[db] = mfma32(va, pl, oacc[db]);
       }
@@ -220,6 +230,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   float m_run = -INFINITY, l_run = 0.f;
 
   const TileLanes<D, kBlkK, NT / 64> tl;
+  const ColFragLanes<D> cf(lane);
   __syncthreads();  // list staged
   auto blk = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[min(t, cnt - 1)]); };
   const u32x4 vsrc = use16 ? v16rs : vrs;
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
       const int jn_v = lst[min(t + 2, cnt - 1)];                                           \
       /* key0 is read by the tail form only */                                            \
       fwd_tile<D, SPLIT, false, V16_>(smem[buf][0], smem[buf][1], 0, N, qf, oacc, m_run,   \
-                                      l_run, scale_log2, lane);                            \
+                                      l_run, scale_log2, lane, cf);                        \
       wait_vmem();                                                                         \
       __syncthreads();                                                                     \
       jn = __builtin_amdgcn_readfirstlane(jn_v);                                           \
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
     if (tail_last) {                                                                       \
       const int buf = cnt_main & 1;                                                        \
       fwd_tile<D, SPLIT, true, V16_>(smem[buf][0], smem[buf][1], blk(cnt_main) * kBlkK, N, \
-                                     qf, oacc, m_run, l_run, scale_log2, lane);            \
+                                     qf, oacc, m_run, l_run, scale_log2, lane, cf);        \
     }                                                                                      \
   }
   // two copies of the loop, one per operand format, so that neither carries the other's

@@ -162,6 +162,52 @@ __device__ __forceinline__ bf16x8 lds_colfrag(const uint16_t* lds, int r0, int c
   return join_bf16x8(lo, hi);
 }
 
+// Per-lane byte offsets, within a tile, of the two transpose reads that gather the
+// operand X[8h + t][c0 + lane%32] (t = 0..7; lds_colfrag with r0 = 0) for each 32-column
+// block c0 = 32 db.  With the row swizzle depending on a row's low four bits only, a read
+// for r0 = 16 kk differs from them by the constant kk * 16 rows, so after one add of the
+// tile's base the reads of every k-step use the instruction's immediate offset.  Computed
+// once per workgroup; the empty asm statements keep the compiler from recomputing them.
+template <int D>
+struct ColFragLanes {
+  static constexpr int DB = D / 32;
+  uint32_t off[DB][2];
+  __device__ __forceinline__ explicit ColFragLanes(int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const int row = 8 * (g >> 1) + (s >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = 32 * db + 16 * (g & 1) + 4 * (s & 3);
+      off[db][0] = (uint32_t)Tile<D>::off(row, col) * 2;
+      off[db][1] = (uint32_t)Tile<D>::off(row + 4, col) * 2;
+      asm volatile("" : "+v"(off[db][0]), "+v"(off[db][1]));
+    }
+  }
+};
+
+// lds_colfrag<D>(tile, 16 * kk, 32 * db, lane) through precomputed lane offsets: base[h] is
+// the tile's LDS byte address plus off[db][h].
+template <int D>
+__device__ __forceinline__ bf16x8 lds_colfrag_at(uint32_t base_lo, uint32_t base_hi, int kk) {
+  const uint32_t step = (uint32_t)kk * 16 * D * 2;
+  const i16x4 lo = lds_read_tr16((const SPA_LDS void*)(uintptr_t)(base_lo + step));
+  const i16x4 hi = lds_read_tr16((const SPA_LDS void*)(uintptr_t)(base_hi + step));
+  return join_bf16x8(lo, hi);
+}
+
+// The per-lane read addresses of a tile whose rows r0 .. r0+31 are read (r0 uniform).
+template <int D>
+__device__ __forceinline__ void colfrag_bases(const uint16_t* tile, int r0,
+                                              const ColFragLanes<D>& cf,
+                                              uint32_t (&lo)[D / 32], uint32_t (&hi)[D / 32]) {
+  const uint32_t b = lds_addr(tile) + (uint32_t)r0 * D * 2;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    lo[db] = b + cf.off[db][0];
+    hi[db] = b + cf.off[db][1];
+  }
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
