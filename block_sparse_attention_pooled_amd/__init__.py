@@ -20,6 +20,7 @@ import os
 __all__ = [
     "SpaError", "load_library", "library_path", "build_mask", "sparse_attn_fwd",
     "sparse_attn_bwd", "mask_workspace_bytes", "bwd_workspace_bytes", "status_string",
+    "build_mask_noalloc", "NOALLOC_SCRATCH_BYTES",
     "SYMBOLS",
 ]
 
@@ -28,10 +29,12 @@ _LIB_NAME = "libspa.so"
 _lib = None
 
 SYMBOLS = ("spa_mask_workspace_bytes", "spa_build_mask", "spa_build_mask_stages",
+           "spa_build_mask_noalloc",
            "spa_fwd_workspace_bytes", "spa_sparse_attn_fwd", "spa_sparse_attn_fwd_stages",
            "spa_bwd_workspace_bytes", "spa_sparse_attn_bwd", "spa_sparse_attn_bwd_stages",
            "spa_status_string", "spa_version")
 MASK_POOL, MASK_SELECT, MASK_ALL = 1, 2, 3
+NOALLOC_SCRATCH_BYTES = 96 << 20  # SPA_NOALLOC_SCRATCH_BYTES
 FWD_PREP, FWD_ATTN, FWD_ALL = 1, 2, 3
 BWD_PREP, BWD_DQ, BWD_DKDV, BWD_ALL = 1, 2, 4, 7
 
@@ -74,6 +77,9 @@ def load_library():
                                           ctypes.c_double, i32p, i32p, i32p, vp, sz,
                                           ctypes.c_uint, vp]
     lib.spa_build_mask_stages.restype = ctypes.c_int
+    lib.spa_build_mask_noalloc.argtypes = [dp, vp, vp, ctypes.c_double, ctypes.c_double,
+                                           ctypes.c_double, i32p, i32p, i32p, vp]
+    lib.spa_build_mask_noalloc.restype = ctypes.c_int
     lib.spa_sparse_attn_fwd.argtypes = [dp, vp, vp, vp, i32p, i32p, ctypes.c_double, vp, vp, vp,
                                         vp, sz, vp]
     lib.spa_sparse_attn_fwd_stages.argtypes = [dp, vp, vp, vp, i32p, i32p, ctypes.c_double, vp,
@@ -216,6 +222,35 @@ def build_mask(q, k, blk_q: int = 128, blk_k: int = 64, k_frac: float = 0.05, p:
                                    _stream(q.device))
     _check("spa_build_mask", rc)
     return (kv_idx, kv_cnt, rl) if rule_len else (kv_idx, kv_cnt)
+
+
+def build_mask_noalloc(q, k, kv_idx, kv_cnt, blk_q: int = 128, blk_k: int = 64,
+                       k_frac: float = 0.05, p: float = 0.9, pooled_scale: float | None = None,
+                       rule_len=None):
+    """build_mask into caller-given outputs through spa_build_mask_noalloc: no workspace,
+    no allocation (the pooled means use the library's fixed device scratch of
+    NOALLOC_SCRATCH_BYTES).  kv_idx int32 [B, H, Nqb, Nkb], kv_cnt int32 [B, H, Nqb] and the
+    optional rule_len int32 [B, H, Nqb, 2] are written in place.  Calls that overlap on one
+    GPU share the scratch and race."""
+    torch = _torch()
+    lib = load_library()
+    _dev_tensor(q, torch.bfloat16, "q")
+    _dev_tensor(k, torch.bfloat16, "k")
+    if q.shape != k.shape or q.dim() != 4:
+        raise ValueError("q and k must both be [B, H, N, d]")
+    if k.device != q.device:
+        raise ValueError("q and k must be on the same device")
+    B, H, N, d = q.shape
+    nqb, nkb = n_blocks(N, blk_q), n_blocks(N, blk_k)
+    _out_tensor(kv_idx, torch.int32, (B, H, nqb, nkb), "kv_idx", q.device)
+    _out_tensor(kv_cnt, torch.int32, (B, H, nqb), "kv_cnt", q.device)
+    if rule_len is not None:
+        _out_tensor(rule_len, torch.int32, (B, H, nqb, 2), "rule_len", q.device)
+    dims = _dims(q.shape, blk_q, blk_k)
+    rc = lib.spa_build_mask_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), float(k_frac),
+                                    float(p), float(pooled_scale or 0.0), _ptr(kv_idx),
+                                    _ptr(kv_cnt), _ptr(rule_len), _stream(q.device))
+    _check("spa_build_mask_noalloc", rc)
 
 
 def sparse_attn_fwd(q, k, v, kv_idx, kv_cnt, blk_q: int = 128, blk_k: int = 64,

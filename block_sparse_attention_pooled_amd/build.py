@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libspa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["mask.hip", "attn_fwd.hip", "attn_bwd.hip", "spa_api.cpp"]
+SOURCES = ["mask.hip", "mask_scratch.hip", "attn_fwd.hip", "attn_bwd.hip", "spa_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

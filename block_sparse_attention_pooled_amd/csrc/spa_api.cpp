@@ -89,6 +89,26 @@ int spa_build_mask_stages(const spa_dims* dims, const void* q, const void* k, do
   return launch_status(spa::launch_mask(a, stages, static_cast<hipStream_t>(stream)));
 }
 
+int spa_build_mask_noalloc(const spa_dims* dims, const void* q, const void* k, double k_frac,
+                           double p, double pooled_scale, int32_t* kv_idx, int32_t* kv_cnt,
+                           int32_t* rule_len, void* stream) {
+  static_assert(spa::kNoallocScratchBytes == (size_t)SPA_NOALLOC_SCRATCH_BYTES,
+                "header and library agree on the scratch size");
+  Geometry g;
+  int rc = check_dims(dims, &g);
+  if (rc != SPA_OK) return rc;
+  if (!q || !k || !kv_idx || !kv_cnt) return SPA_E_NULL;
+  if (bad_frac(k_frac) || bad_frac(p) || std::isnan(pooled_scale) || std::isinf(pooled_scale))
+    return SPA_E_PARAM;
+  const size_t need = spa::mask_workspace_bytes(g);
+  if (need > spa::kNoallocScratchBytes) return SPA_E_SCRATCH;
+  void* ws = nullptr;
+  if (spa::noalloc_scratch(static_cast<hipStream_t>(stream), &ws) != hipSuccess)
+    return SPA_E_SCRATCH;
+  return spa_build_mask_stages(dims, q, k, k_frac, p, pooled_scale, kv_idx, kv_cnt, rule_len, ws,
+                               need, SPA_MASK_ALL, stream);
+}
+
 size_t spa_fwd_workspace_bytes(const spa_dims* dims) {
   Geometry g;
   if (check_dims(dims, &g) != SPA_OK) return 0;
@@ -189,6 +209,7 @@ const char* spa_status_string(int status) {
     case SPA_E_UNSUPPORTED: return "unsupported configuration (d in {64,128}, blk_q in {64,128}, blk_k 64, Nkb <= 2048)";
     case SPA_E_WORKSPACE: return "workspace too small";
     case SPA_E_LAUNCH: return "kernel launch failed";
+    case SPA_E_SCRATCH: return "the fixed device scratch is too small for this problem or not available on the stream's device";
     default: return "unknown status";
   }
 }

@@ -88,4 +88,11 @@ hipError_t launch_bwd(const BwdArgs& a, unsigned stages, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// ---- mask without a caller workspace ------------------------------------------------------
+// Size of the fixed device scratch (SPA_NOALLOC_SCRATCH_BYTES in spa.h).
+constexpr size_t kNoallocScratchBytes = size_t(96) << 20;
+// The current device's address of the fixed scratch (queried once per device).  Fails if
+// `stream` (non-null) belongs to another device.
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
+
 }  // namespace spa

@@ -60,7 +60,9 @@ typedef enum {
   SPA_E_PARAM = -3,       /* k_frac or p outside [0, 1] or NaN; scale NaN or inf     */
   SPA_E_UNSUPPORTED = -4, /* d, blk_q, blk_k or Nkb outside the supported set        */
   SPA_E_WORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes figure     */
-  SPA_E_LAUNCH = -6       /* the HIP runtime reported an error at launch             */
+  SPA_E_LAUNCH = -6,      /* the HIP runtime reported an error at launch             */
+  SPA_E_SCRATCH = -7      /* spa_build_mask_noalloc: the problem needs more than the
+                             fixed scratch, or the scratch is not available            */
 } spa_status;
 
 typedef struct {
@@ -99,6 +101,28 @@ SPA_API size_t spa_mask_workspace_bytes(const spa_dims* dims);
 SPA_API int spa_build_mask(const spa_dims* dims, const void* q, const void* k, double k_frac,
                    double p, double pooled_scale, int32_t* kv_idx, int32_t* kv_cnt,
                    int32_t* rule_len, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the fixed device scratch that spa_build_mask_noalloc uses. */
+#define SPA_NOALLOC_SCRATCH_BYTES (96u << 20)
+
+/*
+ * spa_build_mask without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (minus ws, ws_bytes), results and
+ * validation as spa_build_mask.  The pooled means live in a fixed device array of
+ * SPA_NOALLOC_SCRATCH_BYTES (96 MiB) that every GPU the library runs on holds until the
+ * process ends; a problem whose spa_mask_workspace_bytes exceeds it (B*H*N*d larger than
+ * about 5e8, e.g. more than twice the B=1, H=40, N=75600, d=128 layer) returns
+ * SPA_E_SCRATCH before any launch.  The first call on a device queries the array's address
+ * there (hipGetSymbolAddress; no allocation).  `stream` must belong to the current device
+ * (else SPA_E_SCRATCH).  All calls on one GPU share its array: calls that overlap on one
+ * GPU (different streams, or threads) race and must be ordered by the caller; calls in
+ * sequence on one stream are safe.
+ */
+SPA_API int spa_build_mask_noalloc(const spa_dims* dims, const void* q, const void* k,
+                                   double k_frac, double p, double pooled_scale,
+                                   int32_t* kv_idx, int32_t* kv_cnt, int32_t* rule_len,
+                                   void* stream);
 
 /*
  * Block-sparse attention forward (mindverse article, sections "Block-dünnbesetzte

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         assert spa.status_string(code) not in ("", "unknown status")
     assert spa.status_string(7) == "unknown status"
 
@@ -168,3 +168,25 @@ def test_c_program_is_built_and_links():
     assert r.returncode == 0, r.stderr
     assert "not found" not in r.stdout, r.stdout
     assert "libspa.so" in r.stdout
+
+
+def test_noalloc_mask_validates_before_any_device_call():
+    """spa_build_mask_noalloc: the usual argument checks, and a problem whose mask workspace
+    exceeds the fixed scratch returns SPA_E_SCRATCH, all before any HIP call."""
+    lib = spa.load_library()
+    d = _dims()
+    assert lib.spa_build_mask_noalloc(None, FAKE, FAKE, 0.05, 0.9, 0.0, FAKE, FAKE, None,
+                                      None) == -1
+    assert lib.spa_build_mask_noalloc(ctypes.byref(d), FAKE, None, 0.05, 0.9, 0.0, FAKE, FAKE,
+                                      None, None) == -1
+    assert lib.spa_build_mask_noalloc(ctypes.byref(d), FAKE, FAKE, 1.5, 0.9, 0.0, FAKE, FAKE,
+                                      None, None) == -3
+    assert lib.spa_build_mask_noalloc(ctypes.byref(_dims(d=96)), FAKE, FAKE, 0.05, 0.9, 0.0,
+                                      FAKE, FAKE, None, None) == -4
+    # a valid shape (B*H*N*d < 2^31) whose fp64 pooled means need 189 MB, beyond 96 MiB
+    big = _dims(B=1, H=120, N=131072, d=64)
+    need = lib.spa_mask_workspace_bytes(ctypes.byref(big))
+    assert need > spa.NOALLOC_SCRATCH_BYTES
+    assert lib.spa_build_mask_noalloc(ctypes.byref(big), FAKE, FAKE, 0.05, 0.9, 0.0, FAKE, FAKE,
+                                      None, None) == -7
+    assert "scratch" in spa.status_string(-7)
