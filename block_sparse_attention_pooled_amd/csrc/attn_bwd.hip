@@ -293,6 +293,27 @@ __device__ __forceinline__ void dkdv_dk(const uint16_t* tq, const float* sd, con
   }
 }
 
+// Writes one wavefront's 32 x D block of dK or dV: element e of accumulator db goes to row
+// 8*(e/4) + e%4 (relative to the lane's first row), column 32*db; rows from nrow on are
+// past the end of the sequence.  The row check is taken only in the last key block
+// (tail, uniform over the workgroup), the one block that can hold such rows.
+template <int D, typename T>
+__device__ __forceinline__ void dkdv_store(T* o, const f32x16 (&acc)[D / 32], bool tail,
+                                           int nrow) {
+  if (!tail) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[(8 * (e >> 2) + (e & 3)) * D + 32 * db] = (T)acc[db][e];
+  } else {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (8 * (e >> 2) + (e & 3) < nrow) o[(8 * (e >> 2) + (e & 3)) * D + 32 * db] = (T)acc[db][e];
+  }
+}
+
 template <int D, int BQ>
 __global__ __launch_bounds__(512, 1) void k_dkdv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -472,23 +493,22 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   }
   __syncthreads();
   if (r0 == 0) {
-    void* out = role ? dk_out : dv_out;
     const float f = role ? scale : 1.f;
+    // every partial sum is read before the first store, so that the reads share one wait
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float g = (acc[db][e] + red[(rbase + db * 16 + e) * 64 + lane]) * f;
-        // accumulator element e: key row 8*(e/4) + 4*h + e%4 of this unit's 32 keys, column c
-        const int krow = j * kBlkK + 32 * kh + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (krow < N) {
-          const size_t off = head + (size_t)krow * D + 32 * db + c;
-          if (grad_bf16)
-            reinterpret_cast<__bf16*>(out)[off] = (__bf16)g;
-          else
-            reinterpret_cast<float*>(out)[off] = g;
-        }
-      }
+      for (int e = 0; e < 16; ++e)
+        acc[db][e] = (acc[db][e] + red[(rbase + db * 16 + e) * 64 + lane]) * f;
+    // accumulator element e: key row 8*(e/4) + 4*h + e%4 of this unit's 32 keys, column c;
+    // only the last key block has rows at or beyond N
+    const int krow0 = j * kBlkK + 32 * kh + 4 * h;
+    const size_t base = head + (size_t)krow0 * D + c;
+    void* out = role ? dk_out : dv_out;
+    if (grad_bf16)
+      dkdv_store<D>(reinterpret_cast<__bf16*>(out) + base, acc, tail, N - krow0);
+    else
+      dkdv_store<D>(reinterpret_cast<float*>(out) + base, acc, tail, N - krow0);
   }
 }
 
