@@ -384,8 +384,10 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   wait_vmem();  // stage 0 and the K / V fragments: nothing of the compiler's is pending
   if (role == 1) {  // the consumer waves hold all of this key block's V between them
+    F16Range vr;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) rbits |= f16_range_bits(__builtin_bit_cast(uint4, bf[kk]));
+    for (int kk = 0; kk < KS; ++kk) vr.add(__builtin_bit_cast(uint4, bf[kk]));
+    rbits |= vr.bits();
   }
   rbits = wave_or4(rbits);
   if (lane == 0) wbits[w] = rbits;
@@ -655,12 +657,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   // block of its list)
   uint32_t rbits = 0;
   if (qvalid) {
+    F16Range dr;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const uint4 u = __builtin_bit_cast(uint4, df[kk]);
-      rbits |= f16_range_bits(u);
+      dr.add(u);
       *reinterpret_cast<uint4*>(do16 + qoff + 16 * kk) = bf16x8_bits_to_f16(u);
     }
+    rbits = dr.bits();
   }
   rbits = wave_or4(rbits);
   if (lane == 0) wbits[wv] = rbits;

@@ -278,20 +278,34 @@ __device__ __forceinline__ uint4 bf16x8_bits_to_f16(const uint4& a) {
 //   kF16Big   a value of magnitude 2^-9 or more;
 //   kF16Sub   a nonzero value below 2^-14 (an fp16 subnormal).
 constexpr uint32_t kF16Over = 1u, kF16Big = 2u, kF16Sub = 4u;
-__device__ __forceinline__ uint32_t f16_range_bits(const uint4& a) {
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-  uint32_t r = 0;
+// The classes of many values are read off two running extremes, kept two bf16 values at a
+// time in packed 16-bit integer lanes: the largest magnitude and the smallest magnitude
+// minus one, where a zero wraps to 0xFFFF and so never counts as the smallest.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+struct F16Range {
+  u16x2 mx = {0, 0};
+  u16x2 mn1 = {0xFFFF, 0xFFFF};
+  __device__ __forceinline__ void add(const uint4& a) {
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint32_t m = (w[e] >> (16 * s)) & 0x7FFFu;  // bf16 magnitude bits
-      r |= m >= 0x4780u ? kF16Over : 0u;                // 2^16: next bf16 above 65280
-      r |= m >= 0x3B00u ? kF16Big : 0u;                 // 2^-9
-      r |= (m != 0u && m < 0x3880u) ? kF16Sub : 0u;     // 2^-14
+    for (int e = 0; e < 4; ++e) {
+      const u16x2 m = __builtin_bit_cast(u16x2, w[e] & 0x7FFF7FFFu);  // bf16 magnitude bits
+      mx = __builtin_elementwise_max(mx, m);
+      mn1 = __builtin_elementwise_min(mn1, m - (u16x2){1, 1});
     }
   }
-  return r;
+  __device__ __forceinline__ uint32_t bits() const {
+    const uint32_t hi = mx.x > mx.y ? mx.x : mx.y;
+    const uint32_t lo1 = mn1.x < mn1.y ? mn1.x : mn1.y;
+    return (hi >= 0x4780u ? kF16Over : 0u)     // 2^16: next bf16 above 65280
+           | (hi >= 0x3B00u ? kF16Big : 0u)    // 2^-9
+           | (lo1 < 0x387Fu ? kF16Sub : 0u);   // a nonzero magnitude below 2^-14
+  }
+};
+__device__ __forceinline__ uint32_t f16_range_bits(const uint4& a) {
+  F16Range r;
+  r.add(a);
+  return r.bits();
 }
 
 // A block of values goes through its fp16 copy when nothing is beyond fp16's range and
