@@ -372,17 +372,23 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   for (int x = threadIdx.x; x < cnt; x += 512)
     rbits |= doflag[(size_t)bh * nqb + lst[x]] != 0 ? 8u : 0u;
   if (nst > 0) dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tiles[0], side[0], tl);
-
-  bf16x8 bf[KS];  // producer: K row of this lane's key; consumer: V row
-  {
-    const uint16_t* src_row = (role ? v : k) + head + (size_t)min(key, N - 1) * D + 8 * h;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) bf[kk] = *reinterpret_cast<const bf16x8*>(src_row + 16 * kk);
-  }
+  // this key block's K and V rows, each one contiguous 64-row block, staged whole into the
+  // slot that stage 1 fills only inside the loop (rows at or beyond N read as zeros: their
+  // P is masked); gathering the operand rows straight from memory, 32 bytes of each of 32
+  // rows per load, took three times as long
+  tile_load_lds_rsrc<D, 64, 8>(make_rsrc(k + head, (uint32_t)N * D * 2), j * kBlkK, tiles[1], tl);
+  tile_load_lds_rsrc<D, 64, 8>(make_rsrc(v + head, (uint32_t)N * D * 2), j * kBlkK,
+                               tiles[1] + 64 * D, tl);
   f32x16 acc[DB];  // producer: dV; consumer: dK (unscaled)
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  wait_vmem();  // stage 0 and the K / V fragments: nothing of the compiler's is pending
+  wait_vmem();  // stage 0, K and V: nothing vector-memory is pending inside the loop
+  __syncthreads();
+  bf16x8 bf[KS];  // producer: K row of this lane's key; consumer: V row
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    bf[kk] = *reinterpret_cast<const bf16x8*>(tiles[1] + role * 64 * D +
+                                              Tile<D>::off(32 * kh + c, 16 * kk + 8 * h));
   if (role == 1) {  // the consumer waves hold all of this key block's V between them
     F16Range vr;
 #pragma unroll
