@@ -13,10 +13,11 @@
 //               lse_t * log2(e) for its rows, kept in registers and written out for the
 //               next kernel; then walks its key-block list in ascending order and
 //               accumulates dQ += dS K;
-//   k_dkdv      one workgroup per (b, h, key block): walks its query-block list in
-//               ascending order, recomputes S and P (reading D and lse * log2(e) that k_dq
-//               wrote), accumulates dV += P^T dO and dK += dS^T Q in registers (no atomics,
-//               fixed order).
+//   k_dkdv      one resident workgroup per compute unit, taking (b, h, key block) tiles
+//               from work queues in the dispatch order; per tile it walks the query-block
+//               list in ascending order, recomputes S and P (reading D and lse * log2(e)
+//               that k_dq wrote), accumulates dV += P^T dO and dK += dS^T Q in registers
+//               (fixed order, so which workgroup takes a tile never changes the result).
 // All products are MFMA with fp32 accumulation.  dS (in dQ = dS K and dK = dS^T Q) enters
 // as a bf16 hi + lo pair (about 16 bits): on peaked rows dS is a difference of nearly
 // equal terms, and a single bf16 rounding would be visible in the gradients.  P (in
@@ -51,6 +52,10 @@ __global__ __launch_bounds__(64) void k_bitmap(const int32_t* __restrict__ kv_id
   if (t < nw) bits[((size_t)bh * nw + t) * nqb + i] = words[t];
 }
 
+// k_dkdv's work queues: eight per-XCD ticket counters, one for the remainder, and the
+// count of workgroups that have finished.
+constexpr int kDkdvCounters = 10;
+
 // Column lists, 32 key blocks of one head per workgroup, and the dispatch order of their
 // dK/dV workgroups: within these 32 neighbouring key blocks the longest lists go first
 // (ranked by length, ties by position, so the order is deterministic).  The workgroups
@@ -60,10 +65,12 @@ __global__ __launch_bounds__(64) void k_bitmap(const int32_t* __restrict__ kv_id
 __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ bits, int nqb,
                                                   int nkb, int nw, int32_t* __restrict__ q_idx,
                                                   int32_t* __restrict__ q_cnt,
-                                                  int32_t* __restrict__ order) {
+                                                  int32_t* __restrict__ order,
+                                                  int32_t* __restrict__ ctr) {
   extern __shared__ uint32_t colw[];  // [nqb]
   __shared__ int32_t lens[32];
   const int bh = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
+  if (w == 0 && bh == 0 && t < kDkdvCounters) ctr[t] = 0;  // k_dkdv's work queues
   const uint32_t* src = bits + ((size_t)bh * nw + w) * nqb;
   for (int x = t; x < nqb; x += 256) colw[x] = src[x];
   __syncthreads();
@@ -98,10 +105,13 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
 }
 
 // ------------------------------------------------------------------------------------
-// dK, dV: one workgroup per key block (workgroups in XCD-contiguous order), 8 wavefronts,
-// one workgroup per CU.  The key block's query-block list is walked in stages of 64 query
-// rows; Q and dO of each stage stream into a ring of three LDS slots with direct
-// buffer->LDS loads, one stage ahead.
+// dK, dV: one workgroup of 8 wavefronts per CU, resident for the whole launch: it takes
+// key blocks from work queues (per-XCD contiguous ranges of the dispatch order) until all
+// are done.  A launch of one workgroup per key block paid, per block, the hardware
+// dispatcher's wait for a free CU on each shader engine in turn (1.5k to 8k cycles
+// depending on the engine, measured with per-workgroup clock stamps).  Each key block's
+// query-block list is walked in stages of 64 query rows; Q and dO of each stage stream
+// into a ring of three LDS slots with direct buffer->LDS loads, one stage ahead.
 //
 // The 64 keys x 64 rows of a stage split into four units (32 keys x 32 rows).  Each
 // unit has two wavefronts with different jobs, placed so that they share a SIMD:
@@ -322,7 +332,8 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
     const int32_t* __restrict__ q_idx, const int32_t* __restrict__ q_cnt, int N, int npad,
     int nqb, int nkb, int total, float scale_log2, float scale, void* __restrict__ dk_out,
     void* __restrict__ dv_out, int grad_bf16, const uint16_t* __restrict__ do16,
-    const int32_t* __restrict__ doflag, const int32_t* __restrict__ order) {
+    const int32_t* __restrict__ doflag, const int32_t* __restrict__ order,
+    int32_t* __restrict__ ctr) {
   constexpr int DB = D / 32;
   constexpr int KS = D / 16;
   constexpr int HR = 64;                 // query rows per stage
@@ -336,16 +347,43 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   __shared__ int32_t lst[kMaxBlocks];
   __shared__ uint32_t wbits[8];  // per wavefront: fp16 range classes of V, listed dO flags
   static_assert(2 * DB * 16 * 64 * 4 <= SLOT * 2, "reduction buffer reuses a slot");
+  __shared__ int32_t next_tix;  // the ticket of this workgroup's next key block, or -1
 
-  const int tile_id = order[xcd_remap(blockIdx.x, total)];
-  const int bh = tile_id / nkb;
-  const int j = tile_id - bh * nkb;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31, h = lane >> 5;
   const int role = w >> 2;               // 0 producer, 1 consumer
   const int unit = w & 3;
   const int kh = unit & 1, r0 = 32 * (unit >> 1);
+  const TileLanes<D, 64, 8> tl;
+
+  // Work queues (thread 0 only).  Position t of the dispatch order is ticket t; queue x
+  // (x < 8) hands out the contiguous range [x * per, (x + 1) * per) of positions, queue 8
+  // the remainder.  A workgroup draws from queue blockIdx % 8 (workgroups are dealt to the
+  // XCDs in turn, so each XCD walks one contiguous range, whose neighbouring key blocks
+  // read the same Q and dO tiles), then from the others in turn, so every ticket is taken
+  // once whichever workgroups run.
+  const int whole = total - total % 8, per = whole / 8;
+  const int home = blockIdx.x & 7;
+  int qo = 0;  // queues this workgroup has found empty
+  auto queue = [&](int o) { return o < 8 ? (home + o) & 7 : 8; };
+  auto take = [&](int raw) {  // raw: atomicAdd's result on queue(qo)
+    for (;;) {
+      const int qi = queue(qo);
+      if (raw >= 0 && raw < (qi < 8 ? per : total - whole)) return (qi < 8 ? qi * per : whole) + raw;
+      if (++qo > 8) return -1;
+      raw = atomicAdd(ctr + queue(qo), 1);
+    }
+  };
+  if (threadIdx.x == 0) next_tix = take(atomicAdd(ctr + queue(0), 1));
+  __syncthreads();
+  int tix = __builtin_amdgcn_readfirstlane(next_tix);
+  while (tix >= 0) {
+  int raw_next = 0;
+  if (threadIdx.x == 0 && qo <= 8) raw_next = atomicAdd(ctr + queue(qo), 1);  // lands below
+  const int tile_id = order[tix];
+  const int bh = tile_id / nkb;
+  const int j = tile_id - bh * nkb;
   const size_t head = (size_t)bh * N * D;
   const int key = j * kBlkK + 32 * kh + c;  // this lane's key (B operand column)
   const bool tail = j * kBlkK + kBlkK > N;  // keys at or beyond N exist only here
@@ -363,7 +401,6 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   src.lse2 = make_rsrc(lse2p + (size_t)bh * npad, (uint32_t)npad * 4);
   src.dsum = make_rsrc(dsum + (size_t)bh * npad, (uint32_t)npad * 4);
   for (int x = threadIdx.x; x < cnt; x += 512) lst[x] = list[x];
-  const TileLanes<D, 64, 8> tl;
   __syncthreads();
   auto list_at = [&](int st) {
     return __builtin_amdgcn_readfirstlane(lst[max(0, min(st / HPB, cnt - 1))]);
@@ -383,6 +420,7 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   wait_vmem();  // stage 0, K and V: nothing vector-memory is pending inside the loop
+  if (threadIdx.x == 0) next_tix = qo <= 8 ? take(raw_next) : -1;
   __syncthreads();
   bf16x8 bf[KS];  // producer: K row of this lane's key; consumer: V row
 #pragma unroll
@@ -517,6 +555,14 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
       dkdv_store<D>(reinterpret_cast<__bf16*>(out) + base, acc, tail, N - krow0);
     else
       dkdv_store<D>(reinterpret_cast<float*>(out) + base, acc, tail, N - krow0);
+  }
+  __syncthreads();  // the slots and the list are refilled next
+  tix = __builtin_amdgcn_readfirstlane(next_tix);
+  }
+  // the last workgroup to finish leaves the counters at zero for the next launch
+  if (threadIdx.x == 0 && atomicAdd(ctr + 9, 1) == (int)gridDim.x - 1) {
+#pragma unroll
+    for (int x = 0; x < kDkdvCounters; ++x) ctr[x] = 0;
   }
 }
 
@@ -753,7 +799,8 @@ size_t bwd_workspace_bytes(const Geometry& g) {
          align_up(bh * g.nkb * sizeof(int32_t), 256) +
          align_up(bh * (size_t)g.N * g.d * sizeof(uint16_t), 256) +
          align_up(bh * g.nqb * sizeof(int32_t), 256) +
-         align_up(bh * g.nkb * sizeof(int32_t), 256);
+         align_up(bh * g.nkb * sizeof(int32_t), 256) +
+         align_up(kDkdvCounters * sizeof(int32_t), 256);
 }
 
 void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a) {
@@ -774,6 +821,23 @@ void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a) {
   a->doflag = reinterpret_cast<int32_t*>(p);
   p += align_up(bh * g.nqb * sizeof(int32_t), 256);
   a->order = reinterpret_cast<int32_t*>(p);
+  p += align_up(bh * g.nkb * sizeof(int32_t), 256);
+  a->ctr = reinterpret_cast<int32_t*>(p);
+}
+
+// Compute units of the current device (one dK/dV workgroup fits on each), cached per device.
+static int cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 template <int D, int BQ>
@@ -787,7 +851,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
                        a.kv_cnt, g.nqb, g.nkb, nw, a.bits);
     hipLaunchKernelGGL(k_collists, dim3(nw, (unsigned)g.bh()), dim3(256),
                        g.nqb * sizeof(uint32_t), s, a.bits, g.nqb, g.nkb, nw, a.q_idx, a.q_cnt,
-                       a.order);
+                       a.order, a.ctr);
   }
   if (stages & 2u) {
     const int total = (int)(g.nqb * g.bh());
@@ -798,9 +862,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
   }
   if (stages & 4u) {
     const int total = (int)(g.nkb * g.bh());
-    hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(total), dim3(512), 0, s, a.q, a.k, a.v, a.dout,
+    // one resident workgroup per compute unit, a multiple of 8 so that every XCD holds
+    // as many; each takes key blocks from the queues until all are done
+    const int ncu = cu_count();
+    int grid = ncu - ncu % 8;
+    if (grid < 8) grid = 8;
+    if (grid > total) grid = total;
+    hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(grid), dim3(512), 0, s, a.q, a.k, a.v, a.dout,
                        a.lse2, a.dsum, a.q_idx, a.q_cnt, g.N, npad, g.nqb, g.nkb, total, sl2,
-                       a.scale, a.dk, a.dv, a.grad_bf16, a.do16, a.doflag, a.order);
+                       a.scale, a.dk, a.dv, a.grad_bf16, a.do16, a.doflag, a.order, a.ctr);
   }
   return hipGetLastError();
 }

@@ -79,6 +79,7 @@ struct BwdArgs {
   uint16_t* do16;   // [BH][N][d]: fp16 copy of dO (k_dq writes)
   int32_t* doflag;  // [BH][nqb]: 1 where the block is not read through do16 (k_dq writes)
   int32_t* order;   // [BH * nkb]: dK/dV workgroup dispatch order (k_collists writes)
+  int32_t* ctr;     // [kDkdvCounters]: dK/dV work-queue tickets (k_collists zeroes them)
 };
 size_t bwd_workspace_bytes(const Geometry& g);
 void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a);
