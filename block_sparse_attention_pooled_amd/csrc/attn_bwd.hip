@@ -66,7 +66,8 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
                                                   int nkb, int nw, int32_t* __restrict__ q_idx,
                                                   int32_t* __restrict__ q_cnt,
                                                   int32_t* __restrict__ order,
-                                                  int32_t* __restrict__ ctr) {
+                                                  int32_t* __restrict__ ctr,
+                                                  int32_t* __restrict__ kvflag) {
   extern __shared__ uint32_t colw[];  // [nqb]
   __shared__ int32_t lens[32];
   const int bh = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
     for (int y = 0; y < nb; ++y) rank += (lens[y] > lens[t] || (lens[y] == lens[t] && y < t)) ? 1 : 0;
     const size_t first = (size_t)bh * nkb + w * 32;
     order[first + rank] = (int32_t)(first + t);
+    kvflag[first + t] = 0;  // k_dq sets it where a listed block's dO needs bf16
   }
 }
 
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
     const int32_t* __restrict__ q_idx, const int32_t* __restrict__ q_cnt, int N, int npad,
     int nqb, int nkb, int total, float scale_log2, float scale, void* __restrict__ dk_out,
     void* __restrict__ dv_out, int grad_bf16, const uint16_t* __restrict__ do16,
-    const int32_t* __restrict__ doflag, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ kvflag, const int32_t* __restrict__ order,
     int32_t* __restrict__ ctr) {
   constexpr int DB = D / 32;
   constexpr int KS = D / 16;
@@ -347,7 +349,8 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   __shared__ int32_t lst[kMaxBlocks];
   __shared__ uint32_t wbits[8];  // per wavefront: fp16 range classes of V, listed dO flags
   static_assert(2 * DB * 16 * 64 * 4 <= SLOT * 2, "reduction buffer reuses a slot");
-  __shared__ int32_t next_tix;  // the ticket of this workgroup's next key block, or -1
+  // the next key block: {tile (b*h*nkb + j) or -1, list length, first query block, dO flag}
+  __shared__ int32_t meta[4];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -357,31 +360,49 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   const int kh = unit & 1, r0 = 32 * (unit >> 1);
   const TileLanes<D, 64, 8> tl;
 
-  // Work queues (thread 0 only).  Position t of the dispatch order is ticket t; queue x
-  // (x < 8) hands out the contiguous range [x * per, (x + 1) * per) of positions, queue 8
-  // the remainder.  A workgroup draws from queue blockIdx % 8 (workgroups are dealt to the
-  // XCDs in turn, so each XCD walks one contiguous range, whose neighbouring key blocks
-  // read the same Q and dO tiles), then from the others in turn, so every ticket is taken
-  // once whichever workgroups run.
+  // Work queues, served by one lane (threadIdx 128: wavefront 2, idle while the first
+  // slab's wavefronts write the results).  Position t of the dispatch order is ticket t;
+  // queue x (x < 8) hands out the contiguous range [x * per, (x + 1) * per) of positions,
+  // queue 8 the remainder.  A workgroup draws from queue blockIdx % 8 (workgroups are dealt
+  // to the XCDs in turn, so each XCD walks one contiguous range, whose neighbouring key
+  // blocks read the same Q and dO tiles), then from the others in turn, so every ticket is
+  // taken once whichever workgroups run.
+  constexpr int kQueueLane = 128;
   const int whole = total - total % 8, per = whole / 8;
   const int home = blockIdx.x & 7;
   int qo = 0;  // queues this workgroup has found empty
   auto queue = [&](int o) { return o < 8 ? (home + o) & 7 : 8; };
-  auto take = [&](int raw) {  // raw: atomicAdd's result on queue(qo)
+  // the next ticket's key block and what its prologue needs first, into meta
+  auto fetch_next = [&]() {
+    int raw = atomicAdd(ctr + queue(qo), 1), tix = -1;
     for (;;) {
       const int qi = queue(qo);
-      if (raw >= 0 && raw < (qi < 8 ? per : total - whole)) return (qi < 8 ? qi * per : whole) + raw;
-      if (++qo > 8) return -1;
+      if (raw >= 0 && raw < (qi < 8 ? per : total - whole)) {
+        tix = (qi < 8 ? qi * per : whole) + raw;
+        break;
+      }
+      if (++qo > 8) break;
       raw = atomicAdd(ctr + queue(qo), 1);
     }
+    int tile = -1, n = 0, first = 0, flag = 0;
+    if (tix >= 0) {
+      tile = order[tix];
+      n = q_cnt[tile];
+      first = q_idx[(size_t)tile * nqb];
+      flag = kvflag[tile];
+    }
+    meta[0] = tile;
+    meta[1] = n;
+    meta[2] = first;
+    meta[3] = flag;
   };
-  if (threadIdx.x == 0) next_tix = take(atomicAdd(ctr + queue(0), 1));
+  if (threadIdx.x == kQueueLane) fetch_next();
   __syncthreads();
-  int tix = __builtin_amdgcn_readfirstlane(next_tix);
-  while (tix >= 0) {
-  int raw_next = 0;
-  if (threadIdx.x == 0 && qo <= 8) raw_next = atomicAdd(ctr + queue(qo), 1);  // lands below
-  const int tile_id = order[tix];
+  int tile_id = __builtin_amdgcn_readfirstlane(meta[0]);
+  while (tile_id >= 0) {
+  const int cnt = __builtin_amdgcn_readfirstlane(meta[1]);
+  const int first = __builtin_amdgcn_readfirstlane(meta[2]);
+  const bool do_flag = __builtin_amdgcn_readfirstlane(meta[3]) != 0;
   const int bh = tile_id / nkb;
   const int j = tile_id - bh * nkb;
   const size_t head = (size_t)bh * N * D;
@@ -389,49 +410,49 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   const bool tail = j * kBlkK + kBlkK > N;  // keys at or beyond N exist only here
   const float kmask = key < N ? 1.f : 0.f;
 
-  const int32_t* list = q_idx + ((size_t)bh * nkb + j) * nqb;
-  const int cnt = q_cnt[(size_t)bh * nkb + j];
   const int nst = cnt * HPB;
   DkdvSrc src;
   src.q = make_rsrc(q + head, (uint32_t)N * D * 2);
-  // dO is staged from its fp16 copy unless a listed query block's dO, or this key
-  // block's V, is not to be read through fp16 (f16_block_ok): then from bf16 dO, with P
-  // as a bf16 pair
-  src.dout = make_rsrc(do16 + head, (uint32_t)N * D * 2);
+  // dO is staged from its fp16 copy unless a listed query block's dO (do_flag), or this
+  // key block's V, is not to be read through fp16 (f16_block_ok): then from bf16 dO, with
+  // P as a bf16 pair
+  src.dout = make_rsrc((do_flag ? dout : do16) + head, (uint32_t)N * D * 2);
   src.lse2 = make_rsrc(lse2p + (size_t)bh * npad, (uint32_t)npad * 4);
   src.dsum = make_rsrc(dsum + (size_t)bh * npad, (uint32_t)npad * 4);
-  for (int x = threadIdx.x; x < cnt; x += 512) lst[x] = list[x];
-  __syncthreads();
-  auto list_at = [&](int st) {
-    return __builtin_amdgcn_readfirstlane(lst[max(0, min(st / HPB, cnt - 1))]);
-  };
-  uint32_t rbits = 0;  // bit 3: a listed dO block is flagged; bits 0-2: V range classes
-  for (int x = threadIdx.x; x < cnt; x += 512)
-    rbits |= doflag[(size_t)bh * nqb + lst[x]] != 0 ? 8u : 0u;
-  if (nst > 0) dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tiles[0], side[0], tl);
-  // this key block's K and V rows, each one contiguous 64-row block, staged whole into the
-  // slot that stage 1 fills only inside the loop (rows at or beyond N read as zeros: their
-  // P is masked); gathering the operand rows straight from memory, 32 bytes of each of 32
-  // rows per load, took three times as long
+  // every transfer of the block at once: stage 0, the list (64 entries per wavefront and
+  // transfer; entries past the count read as zeros), and this key block's K and V rows,
+  // each one contiguous 64-row block, into the slot that stage 1 fills only inside the
+  // loop (rows at or beyond N read as zeros: their P is masked).  Gathering the operand
+  // rows straight from memory, 32 bytes of each of 32 rows per load, took three times as
+  // long.
+  if (nst > 0) dkdv_load_stage<D, BQ>(src, first, 0, w, lane, tiles[0], side[0], tl);
+  {
+    const u32x4 lrs = make_rsrc(q_idx + (size_t)tile_id * nqb, (uint32_t)cnt * 4);
+    for (int ch = w; ch * 64 < cnt; ch += 8)
+      dma4(lrs, (uint32_t)(ch * 64 + lane) * 4, 0, lds_addr(lst + ch * 64));
+  }
   tile_load_lds_rsrc<D, 64, 8>(make_rsrc(k + head, (uint32_t)N * D * 2), j * kBlkK, tiles[1], tl);
   tile_load_lds_rsrc<D, 64, 8>(make_rsrc(v + head, (uint32_t)N * D * 2), j * kBlkK,
                                tiles[1] + 64 * D, tl);
   f32x16 acc[DB];  // producer: dV; consumer: dK (unscaled)
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  wait_vmem();  // stage 0, K and V: nothing vector-memory is pending inside the loop
-  if (threadIdx.x == 0) next_tix = qo <= 8 ? take(raw_next) : -1;
+  wait_vmem();  // nothing vector-memory is pending inside the loop
   __syncthreads();
+  auto list_at = [&](int st) {
+    return __builtin_amdgcn_readfirstlane(lst[max(0, min(st / HPB, cnt - 1))]);
+  };
   bf16x8 bf[KS];  // producer: K row of this lane's key; consumer: V row
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
     bf[kk] = *reinterpret_cast<const bf16x8*>(tiles[1] + role * 64 * D +
                                               Tile<D>::off(32 * kh + c, 16 * kk + 8 * h));
+  uint32_t rbits = 0;  // V range classes
   if (role == 1) {  // the consumer waves hold all of this key block's V between them
     F16Range vr;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) vr.add(__builtin_bit_cast(uint4, bf[kk]));
-    rbits |= vr.bits();
+    rbits = vr.bits();
   }
   rbits = wave_or4(rbits);
   if (lane == 0) wbits[w] = rbits;
@@ -439,10 +460,10 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   uint32_t all = 0;
 #pragma unroll
   for (int x = 0; x < 8; ++x) all |= wbits[x];
-  const bool use16 = !(all & 8u) && f16_block_ok(all & 7u);
-  if (!use16) {  // stage 0 again, from bf16 dO
+  const bool use16 = !do_flag && f16_block_ok(all & 7u);
+  if (!use16 && !do_flag) {  // V is not to be read through fp16: stage 0 again, bf16 dO
     src.dout = make_rsrc(dout + head, (uint32_t)N * D * 2);
-    if (nst > 0) dkdv_load_stage<D, BQ>(src, list_at(0), 0, w, lane, tiles[0], side[0], tl);
+    if (nst > 0) dkdv_load_stage<D, BQ>(src, first, 0, w, lane, tiles[0], side[0], tl);
     wait_vmem();
     __syncthreads();
   }
@@ -538,6 +559,8 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
       for (int e = 0; e < 16; ++e) red[(rbase + db * 16 + e) * 64 + lane] = acc[db][e];
   }
   __syncthreads();
+  // the next key block is fetched while the other slab's wavefronts add and write
+  if (threadIdx.x == kQueueLane) fetch_next();
   if (r0 == 0) {
     const float f = role ? scale : 1.f;
     // every partial sum is read before the first store, so that the reads share one wait
@@ -556,8 +579,8 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
     else
       dkdv_store<D>(reinterpret_cast<float*>(out) + base, acc, tail, N - krow0);
   }
-  __syncthreads();  // the slots and the list are refilled next
-  tix = __builtin_amdgcn_readfirstlane(next_tix);
+  __syncthreads();  // the slots and the list are refilled next; meta is written
+  tile_id = __builtin_amdgcn_readfirstlane(meta[0]);
   }
   // the last workgroup to finish leaves the counters at zero for the next launch
   if (threadIdx.x == 0 && atomicAdd(ctr + 9, 1) == (int)gridDim.x - 1) {
@@ -665,7 +688,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     const float* __restrict__ lse, float* __restrict__ lse2p, float* __restrict__ dsum,
     const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt, int N, int npad,
     int nqb, int nkb, int total, float scale_log2, float scale, void* __restrict__ dq_out,
-    int grad_bf16, uint16_t* __restrict__ do16, int32_t* __restrict__ doflag) {
+    int grad_bf16, uint16_t* __restrict__ do16, int32_t* __restrict__ kvflag) {
   constexpr int NT = BQ * 2;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -726,11 +749,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
   __syncthreads();  // list and range bits staged
-  if (threadIdx.x == 0) {
+  {
     uint32_t all = 0;
 #pragma unroll
     for (int x = 0; x < NT / 64; ++x) all |= wbits[x];
-    doflag[(size_t)bh * nqb + i] = f16_block_ok(all) ? 0 : 1;
+    // a block of dO that its fp16 copy does not carry (f16_block_ok): every key block of
+    // this list then takes bf16 dO in k_dkdv
+    if (!f16_block_ok(all))
+      for (int x = threadIdx.x; x < cnt; x += NT) kvflag[(size_t)bh * nkb + lst[x]] = 1;
   }
   if (cnt > 0) {
     const int j0 = blk(0);
@@ -798,7 +824,7 @@ size_t bwd_workspace_bytes(const Geometry& g) {
          align_up(bh * g.nkb * g.nqb * sizeof(int32_t), 256) +
          align_up(bh * g.nkb * sizeof(int32_t), 256) +
          align_up(bh * (size_t)g.N * g.d * sizeof(uint16_t), 256) +
-         align_up(bh * g.nqb * sizeof(int32_t), 256) +
+         align_up(bh * g.nkb * sizeof(int32_t), 256) +
          align_up(bh * g.nkb * sizeof(int32_t), 256) +
          align_up(kDkdvCounters * sizeof(int32_t), 256);
 }
@@ -818,8 +844,8 @@ void bwd_workspace_carve(const Geometry& g, void* ws, BwdArgs* a) {
   p += align_up(bh * g.nkb * sizeof(int32_t), 256);
   a->do16 = reinterpret_cast<uint16_t*>(p);
   p += align_up(bh * (size_t)g.N * g.d * sizeof(uint16_t), 256);
-  a->doflag = reinterpret_cast<int32_t*>(p);
-  p += align_up(bh * g.nqb * sizeof(int32_t), 256);
+  a->kvflag = reinterpret_cast<int32_t*>(p);
+  p += align_up(bh * g.nkb * sizeof(int32_t), 256);
   a->order = reinterpret_cast<int32_t*>(p);
   p += align_up(bh * g.nkb * sizeof(int32_t), 256);
   a->ctr = reinterpret_cast<int32_t*>(p);
@@ -851,14 +877,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
                        a.kv_cnt, g.nqb, g.nkb, nw, a.bits);
     hipLaunchKernelGGL(k_collists, dim3(nw, (unsigned)g.bh()), dim3(256),
                        g.nqb * sizeof(uint32_t), s, a.bits, g.nqb, g.nkb, nw, a.q_idx, a.q_cnt,
-                       a.order, a.ctr);
+                       a.order, a.ctr, a.kvflag);
   }
   if (stages & 2u) {
     const int total = (int)(g.nqb * g.bh());
     hipLaunchKernelGGL((k_dq<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.q, a.k, a.v, a.o,
                        a.o_lo, a.dout, a.lse, a.lse2, a.dsum, a.kv_idx, a.kv_cnt, g.N, npad,
                        g.nqb, g.nkb, total, sl2, a.scale, a.dq, a.grad_bf16, a.do16,
-                       a.doflag);
+                       a.kvflag);
   }
   if (stages & 4u) {
     const int total = (int)(g.nkb * g.bh());
@@ -870,7 +896,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
     if (grid > total) grid = total;
     hipLaunchKernelGGL((k_dkdv<D, BQ>), dim3(grid), dim3(512), 0, s, a.q, a.k, a.v, a.dout,
                        a.lse2, a.dsum, a.q_idx, a.q_cnt, g.N, npad, g.nqb, g.nkb, total, sl2,
-                       a.scale, a.dk, a.dv, a.grad_bf16, a.do16, a.doflag, a.order, a.ctr);
+                       a.scale, a.dk, a.dv, a.grad_bf16, a.do16, a.kvflag, a.order, a.ctr);
   }
   return hipGetLastError();
 }

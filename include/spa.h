@@ -163,9 +163,9 @@ SPA_API size_t spa_fwd_workspace_bytes(const spa_dims* dims);
 /* Bytes of device workspace spa_sparse_attn_bwd needs (D = rowsum(dO*O) and lse*log2(e)
  * per row, padded to whole query blocks, the kept-tile bitmap, the per-key-block
  * query-block lists and their dispatch order, an fp16 copy of dO, one int32 flag per
- * query block and ten int32 work-queue counters of the dK/dV kernel, which SPA_BWD_PREP
- * zeroes and each dK/dV launch leaves at zero; 256-byte aligned sections).  0 for
- * rejected dims. */
+ * key block (a listed query block's dO needs bf16) and ten int32 work-queue counters of
+ * the dK/dV kernel; SPA_BWD_PREP zeroes the flags and the counters, and each dK/dV launch
+ * leaves the counters at zero; 256-byte aligned sections).  0 for rejected dims. */
 SPA_API size_t spa_bwd_workspace_bytes(const spa_dims* dims);
 
 /*

@@ -55,9 +55,9 @@ def test_bwd_workspace_size_formula():
     npad = nqb * 128  # per-row side values (D, lse2) padded to whole query blocks
     want = 2 * B * H * npad * 4 + B * H * (nkb // 32) * nqb * 4 + B * H * nkb * nqb * 4 \
         + B * H * nkb * 4 \
-        + B * H * N * d * 2 + B * H * nqb * 4 \
+        + B * H * N * d * 2 + B * H * nkb * 4 \
         + B * H * nkb * 4 \
-        + 10 * 4  # fp16 copy of dO, flag per query block, dK/dV dispatch order and work queues
+        + 10 * 4  # fp16 copy of dO, dO flag per key block, dK/dV dispatch order and work queues
     got = spa.bwd_workspace_bytes((B, H, N, d), 128, 64)
     assert want <= got <= want + 1024
 
