@@ -276,8 +276,16 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   // ---- epilogue ---------------------------------------------------------------------
   const float l_tot = l_run + swap_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qvalid) {
-    uint16_t* orow = o + head + (size_t)qrow * D;
+  // O and its residual leave through LDS (row-major, Tile swizzle): in the accumulator
+  // layout a store covers 8 bytes of each of 32 rows, while from the staged copy each
+  // wavefront writes whole rows, 16 bytes per lane
+  static_assert(2 * BQ * D <= 4 * Tile<D>::ELEMS, "the output tiles reuse the K and V buffers");
+  const bool with_lo = SPLIT && o_lo != nullptr;
+  uint16_t* ot = &smem[0][0][0];
+  uint16_t* lt = ot + BQ * D;
+  __syncthreads();  // every wavefront is done with the last K and V tiles
+  {
+    const int r = 32 * wv + c;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -290,12 +298,28 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
           hv[e] = (__bf16)x;
           lv[e] = (__bf16)(x - (float)hv[e]);
         }
-        *reinterpret_cast<bf16x4*>(orow + d0) = hv;
-        if (SPLIT && o_lo) *reinterpret_cast<bf16x4*>(o_lo + head + (size_t)qrow * D + d0) = lv;
+        *reinterpret_cast<bf16x4*>(ot + Tile<D>::off(r, d0)) = hv;
+        if (with_lo) *reinterpret_cast<bf16x4*>(lt + Tile<D>::off(r, d0)) = lv;
       }
-    if (h == 0)
-      lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
+  __syncthreads();
+  {
+    constexpr int CPR = Tile<D>::CPR;  // 16-byte chunks per row
+    const int ch = lane % CPR;
+#pragma unroll
+    for (int it = 0; it < 32 * CPR / 64; ++it) {  // this wavefront's 32 rows, 64 / CPR a pass
+      const int r = 32 * wv + it * (64 / CPR) + lane / CPR;
+      const int row = i * BQ + r;
+      if (row < N) {
+        const size_t off = head + (size_t)row * D + 8 * ch;
+        *reinterpret_cast<uint4*>(o + off) = *reinterpret_cast<const uint4*>(ot + Tile<D>::off(r, 8 * ch));
+        if (with_lo)
+          *reinterpret_cast<uint4*>(o_lo + off) = *reinterpret_cast<const uint4*>(lt + Tile<D>::off(r, 8 * ch));
+      }
+    }
+  }
+  if (qvalid && h == 0)
+    lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D, int BQ>
