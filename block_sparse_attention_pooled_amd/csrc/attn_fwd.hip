@@ -206,6 +206,24 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   const int32_t* list = kv_idx + ((size_t)bh * nqb + i) * nkb;
   // the lists are trusted; the clamp only keeps a corrupt count inside the LDS list
   const int cnt = min(max(kv_cnt[(size_t)bh * nqb + i], 0), nkb);
+  const int j0 = cnt > 0 ? list[0] : 0;
+  const TileLanes<D, kBlkK, NT / 64> tl;
+  // the first K and V tiles (V from its fp16 copy unless found unusable below) and this
+  // block's Q rows are requested before the list is staged: Q goes to the second buffer,
+  // which the loop fills only after its first step.  Gathering the Q operand rows straight
+  // from memory (32 bytes of each of 32 rows per load) was slower.  Rows at or beyond N
+  // read as zeros and are never written.
+  if (cnt > 0) {
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0], tl);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(v16rs, j0 * kBlkK, smem[0][1], tl);
+  }
+  {
+    const u32x4 qrs = make_rsrc(q + head, (uint32_t)N * D * 2);
+#pragma unroll
+    for (int hq = 0; hq < BQ / kBlkK; ++hq)
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(qrs, i * BQ + hq * kBlkK,
+                                            &smem[1][0][0] + hq * Tile<D>::ELEMS, tl);
+  }
   int bad16 = 0;
   for (int x = threadIdx.x; x < cnt; x += NT) {
     const int j = list[x];
@@ -213,34 +231,30 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
     if (SPLIT) bad16 |= vflag[(size_t)bh * nkb + min(max(j, 0), nkb - 1)];
   }
   // one operand format for the whole workgroup: fp16 V unless a listed block cannot use it
+  // (the list's loads were issued after the transfers above, so these have landed too)
   const bool use16 = SPLIT && !__syncthreads_or(bad16);
+  if (SPLIT && !use16 && cnt > 0)  // the first V tile again, in bf16
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, j0 * kBlkK, smem[0][1], tl);
 
-  // this lane's query row (B operand of S^T = K Q^T); rows beyond N compute on a copy of
-  // row N-1 and are never written
+  // this lane's query row (B operand of S^T = K Q^T)
   const int qrow = i * BQ + 32 * wv + c;
   const bool qvalid = qrow < N;
-  const uint16_t* qsrc = q + head + (size_t)min(qrow, N - 1) * D + 8 * h;
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qsrc + 16 * kk);
-
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const TileLanes<D, kBlkK, NT / 64> tl;
   const ColFragLanes<D> cf(lane);
-  __syncthreads();  // list staged
   auto blk = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[min(t, cnt - 1)]); };
   const u32x4 vsrc = use16 ? v16rs : vrs;
-  if (cnt > 0) {
-    const int j0 = blk(0);
-    tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0], tl);
-    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vsrc, j0 * kBlkK, smem[0][1], tl);
-  }
-  wait_vmem();  // also the Q fragments: nothing vector-memory is pending inside the loop
+  wait_vmem();  // nothing vector-memory is pending inside the loop
   __syncthreads();
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    qf[kk] = *reinterpret_cast<const bf16x8*>(&smem[1][0][0] +
+                                              Tile<D>::off(32 * wv + c, 16 * kk + 8 * h));
+  __syncthreads();  // Q is in registers before the loop refills its buffer
   const bool tail_last = cnt > 0 && blk(cnt - 1) * kBlkK + kBlkK > N;
   const int cnt_main = cnt - (tail_last ? 1 : 0);
   // the block index of the next tile is read from LDS one tile ahead and taken into a
