@@ -654,32 +654,6 @@ __device__ __forceinline__ void dq_tile(const uint16_t* Ks, const uint16_t* Vs, 
   }
 }
 
-// Per-row side values, for the padded rows of whole query blocks: D = rowsum(dO * O) and
-// lse2 = lse * log2(e).  Rows at or beyond N (padding) get D = 0 and lse2 = +inf, so that
-// their probabilities evaluate to exactly 0 wherever a staged tile holds such a row.
-template <int D>
-__device__ __forceinline__ float row_dsum(const uint16_t* o, const uint16_t* o_lo,
-                                          const bf16x8 (&df)[D / 16], size_t qoff) {
-  float acc = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const uint4 a = *reinterpret_cast<const uint4*>(o + qoff + 16 * kk);
-    uint4 l = make_uint4(0u, 0u, 0u, 0u);
-    if (o_lo) l = *reinterpret_cast<const uint4*>(o_lo + qoff + 16 * kk);
-    const uint4 g = __builtin_bit_cast(uint4, df[kk]);
-    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wl[4] = {l.x, l.y, l.z, l.w};
-    const uint32_t wg[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float o0 = bf16_bits_to_f32(wa[e] & 0xFFFFu) + bf16_bits_to_f32(wl[e] & 0xFFFFu);
-      const float o1 = bf16_bits_to_f32(wa[e] >> 16) + bf16_bits_to_f32(wl[e] >> 16);
-      acc = fmaf(o0, bf16_bits_to_f32(wg[e] & 0xFFFFu), acc);
-      acc = fmaf(o1, bf16_bits_to_f32(wg[e] >> 16), acc);
-    }
-  }
-  return acc + swap_halves(acc);  // the two lanes of a row hold its two column halves
-}
-
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -695,6 +669,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   __shared__ __align__(16) uint16_t smem[2][2][Tile<D>::ELEMS];  // [buf][K|V]
   __shared__ int32_t lst[kMaxBlocks];  // the key-block list (keeps scalar loads out of the loop)
   __shared__ uint32_t wbits[NT / 64];  // fp16 range classes of dO, per wavefront
+  __shared__ float dsh[BQ];            // D of each row of the block
 
   const int tile_id = xcd_remap(blockIdx.x, total);
   const int bh = tile_id / nqb;
@@ -707,8 +682,29 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   const int32_t* list = kv_idx + ((size_t)bh * nqb + i) * nkb;
   // the lists are trusted; the clamp only keeps a corrupt count inside the LDS list
   const int cnt = min(max(kv_cnt[(size_t)bh * nqb + i], 0), nkb);
-  for (int x = threadIdx.x; x < cnt; x += NT) lst[x] = list[x];
+  const int j0 = cnt > 0 ? list[0] : 0;
   const TileLanes<D, kBlkK, NT / 64> tl;
+  // Everything the prologue reads is requested at once: the first K and V tiles, this
+  // block's dO rows (by DMA into the second buffer, which the loop fills only after its
+  // first step; rows at or beyond N read as zeros), the list, the Q rows of this lane, and
+  // O (with its residual) in 16-byte chunks, a row to CPR consecutive lanes.  dO's operand
+  // fragments, D = rowsum(dO * O), the fp16 copy of dO and its range classes then come
+  // from the staged rows: gathering operand rows straight from memory (32 bytes of each
+  // of 32 rows per load) made this prologue several times longer.
+  if (cnt > 0) {
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0], tl);
+    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, j0 * kBlkK, smem[0][1], tl);
+  }
+  uint16_t* dot = &smem[1][0][0];  // dO rows of this block, [BQ][D], Tile swizzle
+  static_assert(BQ * D <= 2 * Tile<D>::ELEMS, "dO rows fit the second buffer");
+  {
+    const u32x4 drs = make_rsrc(dout + head, (uint32_t)N * D * 2);
+#pragma unroll
+    for (int hq = 0; hq < BQ / kBlkK; ++hq)
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(drs, i * BQ + hq * kBlkK, dot + hq * Tile<D>::ELEMS,
+                                            tl);
+  }
+  for (int x = threadIdx.x; x < cnt; x += NT) lst[x] = list[x];
   auto blk = [&](int t) { return __builtin_amdgcn_readfirstlane(lst[min(t, cnt - 1)]); };
 
   const int qrow = i * BQ + 32 * wv + c;
@@ -716,39 +712,70 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   const size_t qoff = head + (size_t)min(qrow, N - 1) * D + 8 * h;
   bf16x8 qf[KS], df[KS];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    qf[kk] = *reinterpret_cast<const bf16x8*>(q + qoff + 16 * kk);
-    df[kk] = *reinterpret_cast<const bf16x8*>(dout + qoff + 16 * kk);
-  }
+  for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(q + qoff + 16 * kk);
   const float lse2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dq_sum = qvalid ? row_dsum<D>(o, o_lo, df, qoff) : 0.f;
-  if (h == 0) {  // padded side arrays for k_dkdv
-    const size_t ri = (size_t)bh * npad + qrow;
-    lse2p[ri] = lse2;
-    dsum[ri] = dq_sum;
-  }
-  // the fp16 copy of this block's dO rows for k_dkdv's dV = P^T dO, and a flag when the
-  // block is not to be read through it (f16_block_ok; k_dkdv then reads bf16 dO for every
-  // block of its list)
-  uint32_t rbits = 0;
-  if (qvalid) {
-    F16Range dr;
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPP = NT / CPR;  // rows per pass of the workgroup
+  constexpr int NP = BQ / RPP;   // passes
+  const int ch = threadIdx.x % CPR, rr = threadIdx.x / CPR;
+  uint4 oc[NP], lc[NP];  // chunk ch of O and O_lo, rows rr + RPP * u
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const uint4 u = __builtin_bit_cast(uint4, df[kk]);
-      dr.add(u);
-      *reinterpret_cast<uint4*>(do16 + qoff + 16 * kk) = bf16x8_bits_to_f16(u);
-    }
-    rbits = dr.bits();
+  for (int u = 0; u < NP; ++u) {
+    const size_t off = head + (size_t)min(i * BQ + rr + RPP * u, N - 1) * D + 8 * ch;
+    oc[u] = *reinterpret_cast<const uint4*>(o + off);
+    lc[u] = o_lo ? *reinterpret_cast<const uint4*>(o_lo + off) : make_uint4(0u, 0u, 0u, 0u);
   }
-  rbits = wave_or4(rbits);
-  if (lane == 0) wbits[wv] = rbits;
 
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-
-  __syncthreads();  // list and range bits staged
+  wait_vmem();  // nothing vector-memory is pending inside the loop
+  __syncthreads();  // dO rows and the list staged
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    df[kk] = *reinterpret_cast<const bf16x8*>(dot + Tile<D>::off(32 * wv + c, 16 * kk + 8 * h));
+  // D in fp32 (O = o + o_lo when the forward pass supplied its residual), the fp16 copy
+  // of dO for k_dkdv's dV = P^T dO, and the copy's range classes
+  F16Range dr;
+  float dpart[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int row = i * BQ + rr + RPP * u;
+    const uint4 g = *reinterpret_cast<const uint4*>(dot + Tile<D>::off(rr + RPP * u, 8 * ch));
+    const uint32_t wa[4] = {oc[u].x, oc[u].y, oc[u].z, oc[u].w};
+    const uint32_t wl[4] = {lc[u].x, lc[u].y, lc[u].z, lc[u].w};
+    const uint32_t wg[4] = {g.x, g.y, g.z, g.w};
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float o0 = bf16_bits_to_f32(wa[e] & 0xFFFFu) + bf16_bits_to_f32(wl[e] & 0xFFFFu);
+      const float o1 = bf16_bits_to_f32(wa[e] >> 16) + bf16_bits_to_f32(wl[e] >> 16);
+      a = fmaf(o0, bf16_bits_to_f32(wg[e] & 0xFFFFu), a);
+      a = fmaf(o1, bf16_bits_to_f32(wg[e] >> 16), a);
+    }
+    dpart[u] = row < N ? a : 0.f;
+    if (row < N) {
+      dr.add(g);
+      *reinterpret_cast<uint4*>(do16 + head + (size_t)row * D + 8 * ch) = bf16x8_bits_to_f16(g);
+    }
+  }
+  // each row's sum over its CPR chunks (lanes that differ in the low bits), a fixed tree
+#pragma unroll
+  for (int u = 0; u < NP; ++u)
+#pragma unroll
+    for (int m = 1; m < CPR; m <<= 1) dpart[u] += __shfl_xor(dpart[u], m, 64);
+  if (ch == 0) {  // padded side arrays for k_dkdv; rows at or beyond N get D = 0
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      dsh[rr + RPP * u] = dpart[u];
+      dsum[(size_t)bh * npad + i * BQ + rr + RPP * u] = dpart[u];
+    }
+  }
+  if (h == 0) lse2p[(size_t)bh * npad + qrow] = lse2;  // +inf past N: P is exactly 0 there
+  const uint32_t rbits = wave_or4(dr.bits());
+  if (lane == 0) wbits[wv] = rbits;
+  __syncthreads();  // D and the range classes staged; the second buffer is free again
+  const float dq_sum = dsh[32 * wv + c];
   {
     uint32_t all = 0;
 #pragma unroll
@@ -758,13 +785,6 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
     if (!f16_block_ok(all))
       for (int x = threadIdx.x; x < cnt; x += NT) kvflag[(size_t)bh * nkb + lst[x]] = 1;
   }
-  if (cnt > 0) {
-    const int j0 = blk(0);
-    tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, j0 * kBlkK, smem[0][0], tl);
-    tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, j0 * kBlkK, smem[0][1], tl);
-  }
-  wait_vmem();  // also the row fragments: nothing vector-memory is pending inside the loop
-  __syncthreads();
   // only the last key block of the list can be partial: it gets its own instantiation of
   // the tile body after the loop, so that the loop carries no per-element selects
   const bool tail_last = cnt > 0 && blk(cnt - 1) * kBlkK + kBlkK > N;
