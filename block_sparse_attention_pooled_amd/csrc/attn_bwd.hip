@@ -489,6 +489,9 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
       cur = nxt;                                                                           \
     }                                                                                      \
   }
+  // the consumer's chain (dP, dS, dK) is the longer one of a stage: it issues first
+  // whenever both wavefronts of a SIMD are ready
+  if (role == 1) __builtin_amdgcn_s_setprio(1);
   if (use16) {
     if (role == 0 && tail) {
       SPA_DKDV_LOOP(if (st < nst) {
@@ -547,6 +550,7 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
     })
   }
 #undef SPA_DKDV_LOOP
+  __builtin_amdgcn_s_setprio(0);
 
   // ---- add the two row slabs (fixed order) and write ------------------------------------
   // [role][DB*16][lane], lane-contiguous; key half 0 in slot 0, key half 1 in slot 1
