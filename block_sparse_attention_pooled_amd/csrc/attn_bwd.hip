@@ -8,6 +8,7 @@
 //   k_collists  per key block j, the ascending list of query blocks that keep j, and the
 //               dispatch order of the dK/dV workgroups (longest lists first within each
 //               run of 32 neighbouring key blocks);
+//   k_vflag     per key block, whether its V may be read through an fp16 copy in dK/dV;
 //   k_dq        one workgroup per (b, h, query block): first D_t = <dO_t, O_t> in fp32
 //               (O = o + o_lo when the forward pass supplied its rounding residual) and
 //               lse_t * log2(e) for its rows, kept in registers and written out for the
@@ -66,8 +67,7 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
                                                   int nkb, int nw, int32_t* __restrict__ q_idx,
                                                   int32_t* __restrict__ q_cnt,
                                                   int32_t* __restrict__ order,
-                                                  int32_t* __restrict__ ctr,
-                                                  int32_t* __restrict__ kvflag) {
+                                                  int32_t* __restrict__ ctr) {
   extern __shared__ uint32_t colw[];  // [nqb]
   __shared__ int32_t lens[32];
   const int bh = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
@@ -102,8 +102,30 @@ __global__ __launch_bounds__(256) void k_collists(const uint32_t* __restrict__ b
     for (int y = 0; y < nb; ++y) rank += (lens[y] > lens[t] || (lens[y] == lens[t] && y < t)) ? 1 : 0;
     const size_t first = (size_t)bh * nkb + w * 32;
     order[first + rank] = (int32_t)(first + t);
-    kvflag[first + t] = 0;  // k_dq sets it where a listed block's dO needs bf16
   }
+}
+
+// The dK/dV pass's fp16 flag of each key block: 1 where its V is not to be read through an
+// fp16 copy (f16_block_ok over the block's 64 rows), else 0; k_dq then also sets it where a
+// listed query block's dO is not.  One workgroup per (b, h, key block), 16-byte loads.
+template <int D>
+__global__ __launch_bounds__(256) void k_vflag(const uint16_t* __restrict__ v, int N, int nkb,
+                                               int32_t* __restrict__ kvflag) {
+  __shared__ uint32_t wbits[4];
+  const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int rows = min(kBlkK, N - j * kBlkK);
+  const uint16_t* vb = v + ((size_t)bh * N + (size_t)j * kBlkK) * D;
+  F16Range r;
+#pragma unroll
+  for (int u = 0; u < kBlkK * D / 8 / 256; ++u) {
+    const int x = t + 256 * u;
+    if (x * 8 < rows * D) r.add(*reinterpret_cast<const uint4*>(vb + 8 * (size_t)x));
+  }
+  const uint32_t wb = wave_or4(r.bits());
+  if ((t & 63) == 0) wbits[t >> 6] = wb;
+  __syncthreads();
+  if (t == 0)
+    kvflag[(size_t)bh * nkb + j] = f16_block_ok(wbits[0] | wbits[1] | wbits[2] | wbits[3]) ? 0 : 1;
 }
 
 // ------------------------------------------------------------------------------------
@@ -348,7 +370,6 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   // the query-block list, staged once: reading it from LDS keeps scalar loads (which
   // complete out of order) out of the loop, so LDS waits can stay partial
   __shared__ int32_t lst[kMaxBlocks];
-  __shared__ uint32_t wbits[8];  // per wavefront: fp16 range classes of V, listed dO flags
   static_assert(2 * DB * 16 * 64 * 4 <= SLOT * 2, "reduction buffer reuses a slot");
   // the next key block: {tile (b*h*nkb + j) or -1, list length, first query block, dO flag}
   __shared__ int32_t meta[4];
@@ -414,27 +435,27 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   const int nst = cnt * HPB;
   DkdvSrc src;
   src.q = make_rsrc(q + head, (uint32_t)N * D * 2);
-  // dO is staged from its fp16 copy unless a listed query block's dO (do_flag), or this
-  // key block's V, is not to be read through fp16 (f16_block_ok): then from bf16 dO, with
-  // P as a bf16 pair
+  // dO is staged from its fp16 copy unless this key block's V or a listed query block's dO
+  // is not to be read through fp16 (do_flag; f16_block_ok): then from bf16 dO, with P as a
+  // bf16 pair
   src.dout = make_rsrc((do_flag ? dout : do16) + head, (uint32_t)N * D * 2);
   src.lse2 = make_rsrc(lse2p + (size_t)bh * npad, (uint32_t)npad * 4);
   src.dsum = make_rsrc(dsum + (size_t)bh * npad, (uint32_t)npad * 4);
   // every transfer of the block at once: stage 0, the list (64 entries per wavefront and
   // transfer; entries past the count read as zeros), and this key block's K and V rows,
-  // each one contiguous 64-row block, into the slot that stage 1 fills only inside the
-  // loop (rows at or beyond N read as zeros: their P is masked).  Gathering the operand
-  // rows straight from memory, 32 bytes of each of 32 rows per load, took three times as
-  // long.
+  // each one contiguous 64-row block, into the slot that the loop fills only in its second
+  // step, after the first step's barrier, by which every wavefront has read its rows
+  // (rows at or beyond N read as zeros: their P is masked).  Gathering the operand rows
+  // straight from memory, 32 bytes of each of 32 rows per load, took three times as long.
   if (nst > 0) dkdv_load_stage<D, BQ>(src, first, 0, w, lane, tiles[0], side[0], tl);
   {
     const u32x4 lrs = make_rsrc(q_idx + (size_t)tile_id * nqb, (uint32_t)cnt * 4);
     for (int ch = w; ch * 64 < cnt; ch += 8)
       dma4(lrs, (uint32_t)(ch * 64 + lane) * 4, 0, lds_addr(lst + ch * 64));
   }
-  tile_load_lds_rsrc<D, 64, 8>(make_rsrc(k + head, (uint32_t)N * D * 2), j * kBlkK, tiles[1], tl);
+  tile_load_lds_rsrc<D, 64, 8>(make_rsrc(k + head, (uint32_t)N * D * 2), j * kBlkK, tiles[2], tl);
   tile_load_lds_rsrc<D, 64, 8>(make_rsrc(v + head, (uint32_t)N * D * 2), j * kBlkK,
-                               tiles[1] + 64 * D, tl);
+                               tiles[2] + 64 * D, tl);
   f32x16 acc[DB];  // producer: dV; consumer: dK (unscaled)
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
@@ -446,28 +467,11 @@ __global__ __launch_bounds__(512, 1) void k_dkdv(
   bf16x8 bf[KS];  // producer: K row of this lane's key; consumer: V row
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
-    bf[kk] = *reinterpret_cast<const bf16x8*>(tiles[1] + role * 64 * D +
+    bf[kk] = *reinterpret_cast<const bf16x8*>(tiles[2] + role * 64 * D +
                                               Tile<D>::off(32 * kh + c, 16 * kk + 8 * h));
-  uint32_t rbits = 0;  // V range classes
-  if (role == 1) {  // the consumer waves hold all of this key block's V between them
-    F16Range vr;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) vr.add(__builtin_bit_cast(uint4, bf[kk]));
-    rbits = vr.bits();
-  }
-  rbits = wave_or4(rbits);
-  if (lane == 0) wbits[w] = rbits;
-  __syncthreads();
-  uint32_t all = 0;
-#pragma unroll
-  for (int x = 0; x < 8; ++x) all |= wbits[x];
-  const bool use16 = !do_flag && f16_block_ok(all & 7u);
-  if (!use16 && !do_flag) {  // V is not to be read through fp16: stage 0 again, bf16 dO
-    src.dout = make_rsrc(dout + head, (uint32_t)N * D * 2);
-    if (nst > 0) dkdv_load_stage<D, BQ>(src, first, 0, w, lane, tiles[0], side[0], tl);
-    wait_vmem();
-    __syncthreads();
-  }
+  // the fp16 dV path, unless the key block's V (classified by k_collists) or a listed
+  // query block's dO (flagged by k_dq) is not to be read through fp16
+  const bool use16 = !do_flag;
 
   // One step: loads of stage st+1 into the next slot, producer on stage st, consumer on
   // stage st-1.  Each job runs its own copy of the loop (same barriers), so that neither
@@ -906,7 +910,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t s)
                        a.kv_cnt, g.nqb, g.nkb, nw, a.bits);
     hipLaunchKernelGGL(k_collists, dim3(nw, (unsigned)g.bh()), dim3(256),
                        g.nqb * sizeof(uint32_t), s, a.bits, g.nqb, g.nkb, nw, a.q_idx, a.q_cnt,
-                       a.order, a.ctr, a.kvflag);
+                       a.order, a.ctr);
+    hipLaunchKernelGGL((k_vflag<D>), dim3(g.nkb, (unsigned)g.bh()), dim3(256), 0, s, a.v, g.N,
+                       g.nkb, a.kvflag);
   }
   if (stages & 2u) {
     const int total = (int)(g.nqb * g.bh());

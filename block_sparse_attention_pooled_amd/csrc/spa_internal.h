@@ -77,8 +77,8 @@ struct BwdArgs {
   int32_t* q_idx;   // [BH][nkb][nqb]
   int32_t* q_cnt;   // [BH][nkb]
   uint16_t* do16;   // [BH][N][d]: fp16 copy of dO (k_dq writes)
-  int32_t* kvflag;  // [BH][nkb]: 1 where a listed query block's dO is not read through
-                    // do16 (k_collists zeroes, k_dq sets)
+  int32_t* kvflag;  // [BH][nkb]: 1 where the key block's V or a listed query block's dO is
+                    // not read through fp16 (k_vflag writes V's, k_dq sets dO's)
   int32_t* order;   // [BH * nkb]: dK/dV workgroup dispatch order (k_collists writes)
   int32_t* ctr;     // [kDkdvCounters]: dK/dV work-queue tickets (k_collists zeroes them)
 };

@@ -209,10 +209,12 @@ SPA_API int spa_sparse_attn_bwd(const spa_dims* dims, const void* q, const void*
  * may run it on a second stream while the mask is built; without o_lo it launches
  * nothing), SPA_FWD_ATTN (the attention; with o_lo it reads what SPA_FWD_PREP wrote from
  * the same V).  Stage bits of spa_sparse_attn_bwd_stages: SPA_BWD_PREP (the
- * per-key-block query-block lists and the order in which their workgroups run, into the
- * workspace; it reads kv_idx and kv_cnt only, so a caller may run it on a second stream
- * once the mask exists, e.g. during the forward), SPA_BWD_DQ (dQ; also writes D and
- * lse * log2(e) of every row and the fp16 copy of dO into the workspace), SPA_BWD_DKDV
+ * per-key-block query-block lists, the order in which their workgroups run and each key
+ * block's fp16 flag of V, into the workspace; it reads kv_idx, kv_cnt and V only, so a
+ * caller may run it on a second stream once the mask exists, e.g. during the forward),
+ * SPA_BWD_DQ (dQ; also writes D and lse * log2(e) of every row and the fp16 copy of dO
+ * into the workspace, and flags the key blocks of query blocks whose dO the copy does not
+ * carry), SPA_BWD_DKDV
  * (dK, dV; reads what the other two wrote).  A zero or unknown stage mask gives
  * SPA_E_PARAM.
  */
