@@ -287,30 +287,47 @@ __device__ __forceinline__ void dkdv_dp16(const bf16x8 (&a)[D / 16], const bf16x
     dp = mfma32h(__builtin_bit_cast(f16x8, a[kk]), __builtin_bit_cast(f16x8, vf[kk]), dp);
 }
 
+// The consumer's per-row D values reach the accumulator elements by a row broadcast: lane
+// l reads the value of slab row side_row(l), and element e of every lane in a 16-lane row
+// takes lane e of that row (DPP row_newbcast, folded into the subtraction), one 4-byte LDS
+// read per lane in place of 64 bytes.  Accumulator element e = 4g + i of the lanes with
+// h = l / 32 holds query row 16 (g / 2) + 8 h + 4 (g % 2) + i of the slab (the order in which
+// the row fragments are read).  The producer keeps its 64-byte lse reads: there the
+// broadcast would cost a move per element, which measured slower than the reads.
+__device__ __forceinline__ int side_row(int lane) {
+  const int n = lane & 15;
+  return 16 * (n >> 3) + 8 * (lane >> 5) + 4 * ((n >> 2) & 1) + (n & 3);
+}
+
+template <int E>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + E, 0xF, 0xF, false));
+}
+
+// dS = P (dP - D), element by element (the broadcast needs a constant lane index).
+template <int E = 0>
+__device__ __forceinline__ void dkdv_ds(f32x16& dp, const f32x4 (&pv)[4], float dl) {
+  if constexpr (E < 16) {
+    dp[E] = pv[E / 4][E % 4] * (dp[E] - row_bcast<E>(dl));
+    dkdv_ds<E + 1>(dp, pv, dl);
+  }
+}
+
 // Consumer, second half: dS = P (dP - D) with P from the producer, dK += dS^T Q.
 template <int D>
 __device__ __forceinline__ void dkdv_dk(const uint16_t* tq, const float* sd, const float* pr,
                                         f32x16& dp, f32x16 (&acc)[D / 32], int r0, int lane) {
   constexpr int DB = D / 32, HR = 64;
-  const int h = lane >> 5;
-  const float* dsv = sd + HR;
-  float4 pv[4], dv4[4];
+  f32x4 pv[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    pv[g] = *reinterpret_cast<const float4*>(pr + (g * 64 + lane) * 4);
-    dv4[g] = *reinterpret_cast<const float4*>(dsv + r0 + 16 * (g >> 1) + 8 * h + 4 * (g & 1));
-  }
+  for (int g = 0; g < 4; ++g) pv[g] = *reinterpret_cast<const f32x4*>(pr + (g * 64 + lane) * 4);
+  const float dl = sd[HR + r0 + side_row(lane)];
   bf16x8 qb[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) qb[db] = lds_colfrag<D>(tq, r0, 32 * db, lane);
   SPA_FENCE();
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    dp[4 * g + 0] = pv[g].x * (dp[4 * g + 0] - dv4[g].x);
-    dp[4 * g + 1] = pv[g].y * (dp[4 * g + 1] - dv4[g].y);
-    dp[4 * g + 2] = pv[g].z * (dp[4 * g + 2] - dv4[g].z);
-    dp[4 * g + 3] = pv[g].w * (dp[4 * g + 3] - dv4[g].w);
-  }
+  dkdv_ds(dp, pv, dl);
   __builtin_amdgcn_s_setprio(0);  // the dK products issue at the producer's priority
 #pragma unroll
   for (int kq = 0; kq < 2; ++kq) {
