@@ -149,6 +149,10 @@ def summarize_trace(trace_csv, title, command) -> str:
             "|---|---|---|---|---|---|"]
     for n in order:
         out.append(f"| `{n}` | " + " | ".join(shape[n]) + " |")
+    out += ["", "The VGPR columns are rocprofv3's `Arch_VGPR_Count` / `Accum_VGPR_Count` fields as "
+            "recorded. On this part they read half of the allocation that the compiler reports "
+            "(`-Rpass-analysis=kernel-resource-usage`): 128 for a kernel built with 256 vector "
+            "registers."]
     return "\n".join(out) + "\n"
 
 
