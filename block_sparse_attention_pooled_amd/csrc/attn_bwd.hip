@@ -820,21 +820,31 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_dq(
   const bool tail_last = cnt > 0 && blk(cnt - 1) * kBlkK + kBlkK > N;
   const int cnt_main = cnt - (tail_last ? 1 : 0);
   // the block index of the next tile is read from LDS one tile ahead and taken into a
-  // scalar register after the barrier, so that no step waits for that read
+  // scalar register after the barrier, so that no step waits for that read; the loop is
+  // unrolled over the two buffers, so that every LDS address in a tile is a loop-invariant
+  // register plus a constant offset
   int jn = cnt > 1 ? blk(1) : 0;
-  for (int t = 0; t < cnt_main; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < cnt) {  // the next tile streams into the other buffer meanwhile
-      tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0], tl);
-      tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, jn * kBlkK, smem[buf ^ 1][1], tl);
-    }
-    const int jn_v = lst[min(t + 2, cnt - 1)];
-    dq_tile<D, false>(smem[buf][0], smem[buf][1], 0 /* read by the tail form only */, N, qf,
-                      df, lse2, dq_sum, acc, scale_log2, lane);
-    wait_vmem();
-    __syncthreads();
-    jn = __builtin_amdgcn_readfirstlane(jn_v);
+#define SPA_DQ_STEP(BUF)                                                                     \
+  {                                                                                        \
+    if (t + 1 < cnt) { /* the next tile streams into the other buffer meanwhile */         \
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[(BUF) ^ 1][0], tl);      \
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(vrs, jn * kBlkK, smem[(BUF) ^ 1][1], tl);      \
+    }                                                                                      \
+    const int jn_v = lst[min(t + 2, cnt - 1)];                                             \
+    dq_tile<D, false>(smem[BUF][0], smem[BUF][1], 0 /* read by the tail form only */, N,   \
+                      qf, df, lse2, dq_sum, acc, scale_log2, lane);                        \
+    wait_vmem();                                                                           \
+    __syncthreads();                                                                       \
+    jn = __builtin_amdgcn_readfirstlane(jn_v);                                             \
   }
+  for (int t = 0;;) {
+    if (t >= cnt_main) break;
+    SPA_DQ_STEP(0)
+    if (++t >= cnt_main) break;
+    SPA_DQ_STEP(1)
+    ++t;
+  }
+#undef SPA_DQ_STEP
   if (tail_last) {
     const int buf = cnt_main & 1;
     dq_tile<D, true>(smem[buf][0], smem[buf][1], blk(cnt_main) * kBlkK, N, qf, df, lse2, dq_sum,

@@ -259,22 +259,31 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   const int cnt_main = cnt - (tail_last ? 1 : 0);
   // the block index of the next tile is read from LDS one tile ahead and taken into a
   // scalar register after the barrier, so that no step waits for that read
+// The loop is unrolled over the two buffers, so that every LDS address in a tile is a
+// loop-invariant register plus a constant offset.
+#define SPA_FWD_STEP(BUF, V16_)                                                              \
+  {                                                                                        \
+    if (t + 1 < cnt) {                                                                     \
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[(BUF) ^ 1][0], tl);      \
+      tile_load_lds_rsrc<D, kBlkK, NT / 64>(vsrc, jn * kBlkK, smem[(BUF) ^ 1][1], tl);     \
+    }                                                                                      \
+    const int jn_v = lst[min(t + 2, cnt - 1)];                                             \
+    /* key0 is read by the tail form only */                                              \
+    fwd_tile<D, SPLIT, false, V16_>(smem[BUF][0], smem[BUF][1], 0, N, qf, oacc, m_run,     \
+                                    l_run, scale_log2, lane, cf);                          \
+    wait_vmem();                                                                           \
+    __syncthreads();                                                                       \
+    jn = __builtin_amdgcn_readfirstlane(jn_v);                                             \
+  }
 #define SPA_FWD_LOOP(V16_)                                                                   \
   {                                                                                        \
     int jn = cnt > 1 ? blk(1) : 0;                                                         \
-    for (int t = 0; t < cnt_main; ++t) {                                                   \
-      const int buf = t & 1;                                                               \
-      if (t + 1 < cnt) {                                                                   \
-        tile_load_lds_rsrc<D, kBlkK, NT / 64>(krs, jn * kBlkK, smem[buf ^ 1][0], tl);      \
-        tile_load_lds_rsrc<D, kBlkK, NT / 64>(vsrc, jn * kBlkK, smem[buf ^ 1][1], tl);     \
-      }                                                                                    \
-      const int jn_v = lst[min(t + 2, cnt - 1)];                                           \
-      /* key0 is read by the tail form only */                                            \
-      fwd_tile<D, SPLIT, false, V16_>(smem[buf][0], smem[buf][1], 0, N, qf, oacc, m_run,   \
-                                      l_run, scale_log2, lane, cf);                        \
-      wait_vmem();                                                                         \
-      __syncthreads();                                                                     \
-      jn = __builtin_amdgcn_readfirstlane(jn_v);                                           \
+    for (int t = 0;;) {                                                                    \
+      if (t >= cnt_main) break;                                                            \
+      SPA_FWD_STEP(0, V16_)                                                                \
+      if (++t >= cnt_main) break;                                                          \
+      SPA_FWD_STEP(1, V16_)                                                                \
+      ++t;                                                                                 \
     }                                                                                      \
     if (tail_last) {                                                                       \
       const int buf = cnt_main & 1;                                                        \
@@ -286,6 +295,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void k_fwd(const uint16_t* __restrict__ 
   // registers
   if (use16) SPA_FWD_LOOP(true) else SPA_FWD_LOOP(false)
 #undef SPA_FWD_LOOP
+#undef SPA_FWD_STEP
 
   // ---- epilogue ---------------------------------------------------------------------
   const float l_tot = l_run + swap_halves(l_run);
