@@ -141,3 +141,27 @@ def test_rule_superset_kept_mass(st):
     # alone can stop at the sink block and lose most of a row's mass
     assert float(mass["k"][:, uni].mean()) < 0.5 < float(mass["union"][:, uni].mean())
     assert float(mass["p"][:, snk].min()) < float(mass["union"][:, snk].min())
+
+
+def test_stress_reruns_bit_identical(st):
+    """Forward and backward twice with the dense rule and with the union at k = 5 %,
+    p = 0.9: every output equal bit for bit (deterministic accumulation orders, and no
+    race in staging lists longer than one workgroup's threads)."""
+    torch, dev = st["torch"], st["dev"]
+    for k_frac, p in ((1.0, 1.0), (0.05, 0.9)):
+        kv_idx, kv_cnt = spa.build_mask(dev["q"], dev["k"], W.blk_q, W.blk_k, k_frac, p)
+        runs = []
+        for _ in range(2):
+            o, lse, o_lo = spa.sparse_attn_fwd(dev["q"], dev["k"], dev["v"], kv_idx, kv_cnt,
+                                               W.blk_q, W.blk_k, with_residual=True)
+            grads = spa.sparse_attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse,
+                                        kv_idx, kv_cnt, W.blk_q, W.blk_k, o_lo=o_lo)
+            # the forward without the residual is a kernel of its own
+            o1, lse1 = spa.sparse_attn_fwd(dev["q"], dev["k"], dev["v"], kv_idx, kv_cnt,
+                                           W.blk_q, W.blk_k)
+            runs.append((o, lse, o_lo) + tuple(grads) + (o1, lse1))
+        torch.cuda.synchronize()
+        log(f"[stress] reruns k={k_frac} p={p}: longest list {int(kv_cnt.max())} blocks")
+        names = ("O", "LSE", "o_lo", "dQ", "dK", "dV", "O (no residual)", "LSE (no residual)")
+        for name, a, b in zip(names, runs[0], runs[1]):
+            assert torch.equal(a, b), (k_frac, p, name)
